@@ -1,0 +1,230 @@
+// C ABI of libattn (declared in include/attn.h): argument validation, choice
+// of kernel and key-range split, workspace handling and launches.
+#include <math.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+
+#include "../../include/attn.h"
+#include "common.h"
+#include "kernels.h"
+
+namespace {
+
+bool verbose() {
+  static int v = -1;
+  if (v < 0) v = getenv("ATTN_VERBOSE") != nullptr;
+  return v != 0;
+}
+
+void say(const char* what, int status) {
+  if (verbose()) fprintf(stderr, "[attn] %s: %s\n", what, attn_status_string(status));
+}
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+int key_tile(int dtype) { return dtype == ATTN_F32 ? attn::f32_keys_per_tile() : attn::mfma_keys_per_tile(); }
+int rows_per_block(int dtype, int D) {
+  return dtype == ATTN_F32 ? attn::f32_rows_per_block() : attn::mfma_rows_per_block(D);
+}
+
+// Split plan: effective split count and keys per split (a multiple of the key tile).
+struct Plan {
+  int n_split;
+  int keys_per_split;
+};
+
+Plan plan_splits(int dtype, int B, int H, int S_q, int S_k, int D, int req) {
+  (void)B; (void)H; (void)D;
+  const int tile = key_tile(dtype);
+  const int n_tiles = (S_k + tile - 1) / tile;
+  int n = 1;
+  if (req > 1) {
+    n = req;
+  } else if (req == 0) {
+    // short query block against a long key range: split the keys so that
+    // many workgroups stream the key range in parallel
+    if (S_q <= 64 && S_k >= 8192) n = (S_k + 4095) / 4096;
+  }
+  if (n > n_tiles) n = n_tiles;
+  if (n > 256) n = 256;
+  if (n < 1) n = 1;
+  const int tiles_per = (n_tiles + n - 1) / n;
+  const int kps = tiles_per * tile;
+  n = (S_k + kps - 1) / kps;          // drop splits that would be empty
+  return Plan{n, kps};
+}
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+size_t ws_bytes(const Plan& p, int B, int H, int S_q, int D) {
+  if (p.n_split <= 1) return 0;
+  const size_t rows = (size_t)p.n_split * B * H * S_q;
+  return round_up(rows * D * sizeof(float), 256) + round_up(rows * sizeof(float), 256);
+}
+
+int check_args(const void* q, const void* k, const void* v, const void* o, const float* lse, int B,
+               int H, int S_q, int S_k, int D, int causal, float scale, int dtype) {
+  if (!q || !k || !v || !o || !lse) return ATTN_ERR_INVALID_ARG;
+  if (B <= 0 || H <= 0 || S_q <= 0 || S_k <= 0 || D <= 0) return ATTN_ERR_INVALID_ARG;
+  if (dtype != ATTN_F32 && dtype != ATTN_F16 && dtype != ATTN_BF16) return ATTN_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return ATTN_ERR_INVALID_ARG;
+  if (!(scale > 0.0f) || !isfinite(scale)) return ATTN_ERR_INVALID_ARG;
+  if (D != 64 && D != 128 && D != 256) return ATTN_ERR_UNSUPPORTED;
+  if (dtype == ATTN_F32 && D == 256) return ATTN_ERR_UNSUPPORTED;
+  if (causal && S_q > S_k) return ATTN_ERR_UNSUPPORTED;
+  // launch grid must fit in 31 bits
+  const long long blocks = (long long)B * H * ((S_q + 31) / 32) * 256;
+  if (blocks > 0x7fffffffLL) return ATTN_ERR_UNSUPPORTED;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
+    return ATTN_ERR_MISALIGNED;
+  return ATTN_OK;
+}
+
+int run_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int S_q,
+            int S_k, int D, int causal, float scale, int dtype, int req_split, void* ws,
+            size_t ws_size, bool own_ws, hipStream_t st) {
+  int rc = check_args(q, k, v, o, lse, B, H, S_q, S_k, D, causal, scale, dtype);
+  if (rc != ATTN_OK) return rc;
+  if (req_split < 0) return ATTN_ERR_INVALID_ARG;
+  const Plan p = plan_splits(dtype, B, H, S_q, S_k, D, req_split);
+  const size_t need = ws_bytes(p, B, H, S_q, D);
+  if (!own_ws && need > 0 && (ws == nullptr || ws_size < need || !aligned(ws, 256)))
+    return ATTN_ERR_WORKSPACE;
+
+  attn::FwdArgs a;
+  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
+  a.B = B; a.H = H; a.S_q = S_q; a.S_k = S_k; a.D = D;
+  a.causal = causal; a.dtype = dtype;
+  a.n_split = p.n_split; a.keys_per_split = p.keys_per_split;
+  a.c = scale * attn::kLog2e;
+  a.opart = nullptr; a.lpart = nullptr;
+
+  void* buf = ws;
+  if (need > 0) {
+    if (own_ws) {
+      if (hipMallocAsync(&buf, need, st) != hipSuccess) return ATTN_ERR_LAUNCH;
+    }
+    const size_t rows = (size_t)p.n_split * B * H * S_q;
+    a.opart = (float*)buf;
+    a.lpart = (float*)((char*)buf + round_up(rows * D * sizeof(float), 256));
+  }
+  hipError_t e;
+  if (dtype == ATTN_F32) e = attn::launch_fwd_f32(a, st);
+  else if (p.n_split > 1 && S_q <= attn::decode_max_rows()) e = attn::launch_fwd_decode(a, st);
+  else e = attn::launch_fwd_mfma(a, st);
+  if (e == hipSuccess && p.n_split > 1) e = attn::launch_combine(a, st);
+  if (need > 0 && own_ws) {
+    if (hipFreeAsync(buf, st) != hipSuccess && e == hipSuccess) e = hipErrorUnknown;
+  }
+  if (e != hipSuccess) {
+    if (verbose()) fprintf(stderr, "[attn] launch failed: %s\n", hipGetErrorString(e));
+    return ATTN_ERR_LAUNCH;
+  }
+  return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_abi_version(void) { return ATTN_ABI_VERSION; }
+
+const char* attn_status_string(int status) {
+  switch (status) {
+    case ATTN_OK: return "ok";
+    case ATTN_ERR_INVALID_ARG: return "invalid argument";
+    case ATTN_ERR_UNSUPPORTED: return "unsupported configuration";
+    case ATTN_ERR_MISALIGNED: return "misaligned pointer";
+    case ATTN_ERR_LAUNCH: return "HIP launch failure";
+    case ATTN_ERR_WORKSPACE: return "workspace missing or too small";
+  }
+  return "unknown status";
+}
+
+int attn_check_args(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                    int B, int H, int S_q, int S_k, int D, int causal, float scale, int dtype) {
+  return check_args(q, k, v, o, lse, B, H, S_q, S_k, D, causal, scale, dtype);
+}
+
+int attn_fwd_num_splits(int B, int H, int S_q, int S_k, int D, int num_splits) {
+  if (B <= 0 || H <= 0 || S_q <= 0 || S_k <= 0 || num_splits < 0) return 1;
+  return plan_splits(ATTN_BF16, B, H, S_q, S_k, D, num_splits).n_split;
+}
+
+size_t attn_fwd_workspace_size(int B, int H, int S_q, int S_k, int D, int num_splits) {
+  if (B <= 0 || H <= 0 || S_q <= 0 || S_k <= 0 || D <= 0 || num_splits < 0) return 0;
+  // the float32 kernel uses a smaller key tile and can need more splits
+  const Plan a = plan_splits(ATTN_BF16, B, H, S_q, S_k, D, num_splits);
+  const Plan b = plan_splits(ATTN_F32, B, H, S_q, S_k, D, num_splits);
+  const size_t x = ws_bytes(a, B, H, S_q, D), y = ws_bytes(b, B, H, S_q, D);
+  return x > y ? x : y;
+}
+
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+             int S_q, int S_k, int D, int causal, float scale, int dtype, void* stream) {
+  const int rc = run_fwd(q, k, v, o, lse, B, H, S_q, S_k, D, causal, scale, dtype, 0, nullptr, 0,
+                         true, (hipStream_t)stream);
+  if (rc != ATTN_OK) say("attn_fwd", rc);
+  return rc;
+}
+
+int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                int S_q, int S_k, int D, int causal, float scale, int dtype, int num_splits,
+                void* workspace, size_t workspace_bytes, void* stream) {
+  const int rc = run_fwd(q, k, v, o, lse, B, H, S_q, S_k, D, causal, scale, dtype, num_splits,
+                         workspace, workspace_bytes, false, (hipStream_t)stream);
+  if (rc != ATTN_OK) say("attn_fwd_ex", rc);
+  return rc;
+}
+
+int hadamard_quant(const void* x, void* x8, float* scales, const signed char* signs, int B, int H,
+                   int S, int D, int block_rows, int apply_hadamard, int in_dtype, void* stream) {
+  if (!x || !x8 || !scales || !signs) return ATTN_ERR_INVALID_ARG;
+  if (B <= 0 || H <= 0 || S <= 0 || D <= 0 || block_rows <= 0 || block_rows > 1024)
+    return ATTN_ERR_INVALID_ARG;
+  if (apply_hadamard != 0 && apply_hadamard != 1) return ATTN_ERR_INVALID_ARG;
+  if (in_dtype != ATTN_BF16 && in_dtype != ATTN_F16) return ATTN_ERR_INVALID_ARG;
+  if (D != 64 && D != 128 && D != 256) return ATTN_ERR_UNSUPPORTED;
+  if (!aligned(x, 16) || !aligned(x8, 16) || !aligned(scales, 4)) return ATTN_ERR_MISALIGNED;
+  const hipError_t e = attn::launch_hadamard_quant(x, x8, scales, signs, B, H, S, D, block_rows,
+                                                   apply_hadamard, in_dtype, (hipStream_t)stream);
+  return e == hipSuccess ? ATTN_OK : (e == hipErrorNotSupported ? ATTN_ERR_UNSUPPORTED : ATTN_ERR_LAUNCH);
+}
+
+int quant_per_tensor(const void* x, void* x8, float* scale, int B, int H, int S, int D, int in_dtype,
+                     int write_transposed, void* stream) {
+  if (!x || !x8 || !scale) return ATTN_ERR_INVALID_ARG;
+  if (B <= 0 || H <= 0 || S <= 0 || D <= 0) return ATTN_ERR_INVALID_ARG;
+  if (in_dtype != ATTN_BF16 && in_dtype != ATTN_F16) return ATTN_ERR_INVALID_ARG;
+  if (write_transposed != 0 && write_transposed != 1) return ATTN_ERR_INVALID_ARG;
+  if (D % 8 != 0) return ATTN_ERR_UNSUPPORTED;
+  if (write_transposed && S % 16 != 0) return ATTN_ERR_UNSUPPORTED;
+  if (!aligned(x, 16) || !aligned(x8, 16) || !aligned(scale, 4)) return ATTN_ERR_MISALIGNED;
+  const hipError_t e = attn::launch_quant_per_tensor(x, x8, scale, B, H, S, D, in_dtype,
+                                                     write_transposed, (hipStream_t)stream);
+  return e == hipSuccess ? ATTN_OK : (e == hipErrorNotSupported ? ATTN_ERR_UNSUPPORTED : ATTN_ERR_LAUNCH);
+}
+
+int attn_fwd_fp8(const void* q8, const void* k8, const void* v8, const float* q_scales,
+                 const float* k_scales, const float* v_scale, void* o, float* lse, int B, int H,
+                 int S_q, int S_k, int D, int causal, float scale, int block_rows, int v_transposed,
+                 void* stream) {
+  if (!q8 || !k8 || !v8 || !q_scales || !k_scales || !v_scale || !o || !lse) return ATTN_ERR_INVALID_ARG;
+  if (B <= 0 || H <= 0 || S_q <= 0 || S_k <= 0 || D <= 0) return ATTN_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return ATTN_ERR_INVALID_ARG;
+  if (v_transposed != 0 && v_transposed != 1) return ATTN_ERR_INVALID_ARG;
+  if (!(scale > 0.0f) || !isfinite(scale)) return ATTN_ERR_INVALID_ARG;
+  if (D != 128 || block_rows != 64) return ATTN_ERR_UNSUPPORTED;
+  if (causal && S_q > S_k) return ATTN_ERR_UNSUPPORTED;
+  if (v_transposed && S_k % 16 != 0) return ATTN_ERR_UNSUPPORTED;
+  if (!aligned(q8, 16) || !aligned(k8, 16) || !aligned(v8, 16) || !aligned(o, 16) || !aligned(lse, 4) ||
+      !aligned(q_scales, 4) || !aligned(k_scales, 4) || !aligned(v_scale, 4))
+    return ATTN_ERR_MISALIGNED;
+  const hipError_t e = attn::launch_fwd_fp8(q8, k8, v8, q_scales, k_scales, v_scale, o, lse, B, H, S_q,
+                                            S_k, D, causal, scale * attn::kLog2e, v_transposed,
+                                            (hipStream_t)stream);
+  return e == hipSuccess ? ATTN_OK : (e == hipErrorNotSupported ? ATTN_ERR_UNSUPPORTED : ATTN_ERR_LAUNCH);
+}
+
+}  // extern "C"

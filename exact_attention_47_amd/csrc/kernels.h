@@ -1,0 +1,54 @@
+// Host-side view of the kernels: argument bundles and launch functions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace attn {
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  float* opart;        // [n_split][B*H][S_q][D] float32, when n_split > 1
+  float* lpart;        // [n_split][B*H][S_q] float32, when n_split > 1
+  int B, H, S_q, S_k, D;
+  int causal;
+  int dtype;           // ATTN_F32 / ATTN_F16 / ATTN_BF16
+  int n_split;         // >= 1
+  int keys_per_split;  // multiple of the kernel's key tile
+  float c;             // scale * log2(e)
+};
+
+// bf16 / fp16 matrix-core kernel
+hipError_t launch_fwd_mfma(const FwdArgs& a, hipStream_t st);
+int mfma_rows_per_block(int D);
+int mfma_keys_per_tile();
+
+// float32 kernel
+hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t st);
+int f32_rows_per_block();
+int f32_keys_per_tile();
+
+// single-query-row decode kernel (S_q small, long key range)
+hipError_t launch_fwd_decode(const FwdArgs& a, hipStream_t st);
+int decode_keys_per_tile();
+int decode_max_rows();
+
+// merge of split partials into O (dtype) and LSE
+hipError_t launch_combine(const FwdArgs& a, hipStream_t st);
+
+// FP8 path
+hipError_t launch_hadamard_quant(const void* x, void* x8, float* scales, const signed char* signs,
+                                 int B, int H, int S, int D, int block_rows, int apply_hadamard,
+                                 int in_dtype, hipStream_t st);
+hipError_t launch_quant_per_tensor(const void* x, void* x8, float* scale, int B, int H, int S, int D,
+                                   int in_dtype, int write_transposed, hipStream_t st);
+hipError_t launch_fwd_fp8(const void* q8, const void* k8, const void* v8, const float* qs,
+                          const float* ks, const float* vs, void* o, float* lse, int B, int H,
+                          int S_q, int S_k, int D, int causal, float c, int v_transposed,
+                          hipStream_t st);
+
+}  // namespace attn

@@ -1,0 +1,188 @@
+/*
+ * attn.h -- C ABI of libattn, the exact fused attention forward pass for
+ * AMD MI355X (gfx950).
+ *
+ * Sources (cited by page title and section):
+ *   [NL] "FlashAttention-3 (NL)", systems-analysis.info
+ *   [GN] "FlashAttention-3: Schnellere und praezisere Attention durch
+ *        Asynchronitaet und geringe Praezision", GeekNews (de.news.hada.io)
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Tensors are contiguous [B, H, S, D] with D innermost (element (b,h,s,d)
+ *    at ((b*H + h)*S + s)*D + d). LSE is contiguous [B, H, S_q] float32.
+ *  - Every pointer is a device pointer allocated by the caller, who owns it.
+ *    The library never frees caller memory and keeps no state between calls.
+ *  - `stream` is a hipStream_t passed as an opaque pointer (NULL = the null
+ *    stream). Every call only enqueues work on it and returns; nothing is
+ *    synchronised inside the library.
+ *  - Return value: ATTN_OK or a negative status. On any error status nothing
+ *    has been enqueued and no output has been touched, except ATTN_ERR_LAUNCH,
+ *    which reports a failure of the HIP runtime at launch time.
+ *  - Device pointers must be 16-byte aligned; sizes must be positive.
+ *  - Results are bitwise deterministic for fixed inputs and arguments (no
+ *    atomics whose order can change a floating-point result).
+ */
+#ifndef ATTN_H
+#define ATTN_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ATTN_ABI_VERSION 1
+
+/* element types */
+#define ATTN_F32  0
+#define ATTN_F16  1
+#define ATTN_BF16 2
+
+/* status codes */
+#define ATTN_OK                0
+#define ATTN_ERR_INVALID_ARG  (-1) /* null pointer, non-positive size, unknown dtype */
+#define ATTN_ERR_UNSUPPORTED  (-2) /* valid but not implemented: D not in {64,128,256}, causal with S_q > S_k, ... */
+#define ATTN_ERR_MISALIGNED   (-3) /* a device pointer is not 16-byte aligned */
+#define ATTN_ERR_LAUNCH       (-4) /* the HIP runtime reported an error when enqueuing */
+#define ATTN_ERR_WORKSPACE    (-5) /* workspace missing or smaller than attn_fwd_workspace_size() */
+
+/* Version of this interface (ATTN_ABI_VERSION). */
+int attn_abi_version(void);
+
+/* Static, human-readable text for a status code. */
+const char* attn_status_string(int status);
+
+/*
+ * attn_fwd -- O = softmax(scale * Q K^T [+ causal mask]) V and its row-wise
+ * logsumexp, computed tile by tile with online softmax rescaling so that the
+ * S_q x S_k score matrix never reaches device memory.
+ *
+ * Defined by: the attention computation of [NL] "Het probleem van het
+ * aandachtsmechanisme"; the tiled, fused, exact method of [NL] "FlashAttention
+ * en FlashAttention-2" and [GN] "Rueckblick auf den FlashAttention-Ansatz".
+ *
+ *   q      [B, H, S_q, D]   dtype
+ *   k, v   [B, H, S_k, D]   dtype
+ *   o      [B, H, S_q, D]   dtype (written)
+ *   lse    [B, H, S_q]      float32 (written): natural-log logsumexp of the
+ *                           scaled, masked scores of each query row
+ *   causal 0 or 1: key j is allowed for query i iff j <= i + (S_k - S_q)
+ *          (bottom-right aligned); causal with S_q > S_k is ATTN_ERR_UNSUPPORTED
+ *   scale  multiplier of Q K^T (commonly 1/sqrt(D)); must be finite and > 0
+ *   dtype  ATTN_F32, ATTN_F16 or ATTN_BF16; accumulation is float32 in all cases
+ *   D      64, 128 or 256 (ATTN_F32: 64 or 128)
+ *
+ * For short query lengths with long key ranges the library splits the key
+ * range and merges the partial results by logsumexp; the temporary buffer it
+ * needs is taken from the stream-ordered allocator on `stream` and released
+ * on the same stream.
+ */
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+             int B, int H, int S_q, int S_k, int D, int causal, float scale,
+             int dtype, void* stream);
+
+/*
+ * attn_fwd_ex -- attn_fwd with explicit control of the key-range split.
+ *
+ *   num_splits  0 = choose automatically (as attn_fwd), 1 = never split,
+ *               n > 1 = split the key range into n near-equal chunks
+ *               (clamped to the number of key tiles)
+ *   workspace   device buffer of at least
+ *               attn_fwd_workspace_size(B, H, S_q, S_k, D, num_splits) bytes,
+ *               used when the effective split count is > 1; may be NULL when
+ *               no split happens. Partial outputs (float32) and partial LSEs
+ *               are staged there; it holds no state after the call.
+ */
+int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
+                int B, int H, int S_q, int S_k, int D, int causal, float scale,
+                int dtype, int num_splits, void* workspace, size_t workspace_bytes,
+                void* stream);
+
+/* Bytes of workspace attn_fwd_ex needs for these sizes and split request
+ * (0 when the effective split count is 1). num_splits = 0 means "automatic". */
+size_t attn_fwd_workspace_size(int B, int H, int S_q, int S_k, int D, int num_splits);
+
+/* The split count attn_fwd would use (or attn_fwd_ex with num_splits), after
+ * clamping; 1 means no split. Host-only, never touches the device. */
+int attn_fwd_num_splits(int B, int H, int S_q, int S_k, int D, int num_splits);
+
+/*
+ * attn_check_args -- the argument validation attn_fwd performs, without
+ * enqueuing anything. Returns the status attn_fwd would return for these
+ * arguments if the launch itself succeeded. Host-only.
+ */
+int attn_check_args(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                    int B, int H, int S_q, int S_k, int D, int causal, float scale, int dtype);
+
+/*
+ * hadamard_quant -- incoherent processing for FP8: x' = H_D diag(signs) x /
+ * sqrt(D) along D for every row, then E4M3 quantization with one scale per
+ * block of `block_rows` consecutive rows of each (b, h).
+ *
+ * Defined by: [NL] "3. Lage precisie (FP8) met reductie van kwantisatiefout"
+ * (multiply Q and K by a random orthogonal matrix before quantizing) and
+ * [GN] "Niedrige FP8-Praezision und incoherent processing" (random-sign
+ * Hadamard, O(d log d) per head, memory-bound).
+ *
+ *   x        [B, H, S, D] in_dtype (ATTN_BF16 or ATTN_F16)
+ *   x8       [B, H, S, D] uint8 E4M3 codes (written)
+ *   scales   [B, H, ceil(S / block_rows)] float32 (written): dequantized
+ *            value = E4M3(code) * scale of the code's block
+ *   signs    device int8[D], every entry +1 or -1 (values are not checked)
+ *   block_rows  1..1024
+ *   apply_hadamard  1: transform then quantize; 0: quantize x itself
+ *
+ * Arithmetic (all float32, so the codes are unique): u = FWHT(signs * x) with
+ * butterfly strides 1, 2, ..., D/2 (unnormalised); per block a = max |u|;
+ * inv = 448 / a; code = E4M3_RNE(u * inv) (saturating); scale = a / 448,
+ * then scale *= 1/sqrt(D) when the transform is applied. A block with a == 0
+ * gets scale 1 and codes 0. D in {64, 128, 256}.
+ */
+int hadamard_quant(const void* x, void* x8, float* scales, const signed char* signs,
+                   int B, int H, int S, int D, int block_rows, int apply_hadamard,
+                   int in_dtype, void* stream);
+
+/*
+ * quant_per_tensor -- E4M3 quantization with one scale for the whole tensor
+ * (two launches: max |x|, then quantize). Used for V on the FP8 path and for
+ * the plain per-tensor FP8 baseline without a transform.
+ *
+ *   x       [B, H, S, D] in_dtype (ATTN_BF16 or ATTN_F16)
+ *   x8      uint8 E4M3 codes (written), [B, H, S, D], or [B, H, D, S] when
+ *           write_transposed = 1
+ *   scale   one device float32 (written): a / 448 with a = max |x|, 1 if a == 0;
+ *           it also serves as the reduction target and is cleared on-stream first
+ *   code = E4M3_RNE(x * (448 / a)), saturating.
+ */
+int quant_per_tensor(const void* x, void* x8, float* scale, int B, int H, int S, int D,
+                     int in_dtype, int write_transposed, void* stream);
+
+/*
+ * attn_fwd_fp8 -- attention on E4M3 inputs with float32 accumulation,
+ * bfloat16 output and float32 LSE ([NL] "3. Lage precisie (FP8) met reductie
+ * van kwantisatiefout"; [GN] "Niedrige FP8-Praezision und incoherent
+ * processing").
+ *
+ *   q8, k8      [B, H, S_q|S_k, D] E4M3 codes
+ *   q_scales    [B, H, ceil(S_q / block_rows)] float32 block scales of q8
+ *   k_scales    [B, H, ceil(S_k / block_rows)] float32 block scales of k8
+ *   v8          E4M3 codes of V, [B, H, S_k, D] (v_transposed = 0) or
+ *               [B, H, D, S_k] (v_transposed = 1)
+ *   v_scale     one device float32: the per-tensor scale of v8
+ *   o           [B, H, S_q, D] bfloat16 (written); lse [B, H, S_q] float32
+ *   block_rows  must be 64 (the key tile of the kernel)
+ * Scores are scale * (q8 . k8) * q_scale(row block) * k_scale(key block).
+ * The probabilities entering P V are rounded to E4M3 after multiplication by
+ * 2^8; the row sums use the unrounded values. D = 128.
+ */
+int attn_fwd_fp8(const void* q8, const void* k8, const void* v8,
+                 const float* q_scales, const float* k_scales, const float* v_scale,
+                 void* o, float* lse, int B, int H, int S_q, int S_k, int D,
+                 int causal, float scale, int block_rows, int v_transposed, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_H */

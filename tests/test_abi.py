@@ -1,0 +1,99 @@
+"""CPU checks of the C ABI: the library loads, exports every declared entry point,
+and its host-only functions (validation, split plan, status text) behave as the
+header states. Nothing here launches a kernel."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from exact_attention_47_amd import attn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b([a-z_][a-z0-9_]*)\s*\(", text, flags=re.M)
+    return sorted(set(n for n in names if n not in ("if", "defined")))
+
+
+def test_header_declares_the_expected_api():
+    names = declared_functions()
+    for n in ("attn_fwd", "attn_fwd_ex", "attn_fwd_workspace_size", "hadamard_quant",
+              "quant_per_tensor", "attn_fwd_fp8", "attn_status_string", "attn_abi_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(attn.LIB_PATH)
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert missing == []
+
+
+def test_binding_signatures_cover_every_declared_symbol():
+    assert sorted(attn._SIGS) == declared_functions()
+
+
+def test_version_and_status_strings():
+    assert attn.abi_version() == 1
+    lib = attn.load()
+    for code in (0, -1, -2, -3, -4, -5):
+        assert lib.attn_status_string(code).decode() not in ("", "unknown status")
+    assert lib.attn_status_string(-99).decode() == "unknown status"
+
+
+P = 0x10000  # fake, 16-byte aligned "device" addresses: validation never dereferences them
+
+
+def chk(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=1, H=2, S_q=128, S_k=128, D=128, causal=0, scale=0.125, dtype=2)
+    a.update(kw)
+    return attn.check_args(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["S_q"], a["S_k"],
+                           a["D"], a["causal"], a["scale"], a["dtype"])
+
+
+def test_validation_accepts_good_arguments():
+    assert chk() == attn.OK
+    for d in (64, 128, 256):
+        assert chk(D=d) == attn.OK
+    assert chk(dtype=0, D=64) == attn.OK
+    assert chk(causal=1, S_q=100, S_k=300) == attn.OK
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), attn.ERR_INVALID_ARG),
+    (dict(lse=None), attn.ERR_INVALID_ARG),
+    (dict(B=0), attn.ERR_INVALID_ARG),
+    (dict(S_k=-1), attn.ERR_INVALID_ARG),
+    (dict(dtype=7), attn.ERR_INVALID_ARG),
+    (dict(causal=2), attn.ERR_INVALID_ARG),
+    (dict(scale=0.0), attn.ERR_INVALID_ARG),
+    (dict(scale=float("nan")), attn.ERR_INVALID_ARG),
+    (dict(scale=float("inf")), attn.ERR_INVALID_ARG),
+    (dict(D=96), attn.ERR_UNSUPPORTED),
+    (dict(D=32), attn.ERR_UNSUPPORTED),
+    (dict(dtype=0, D=256), attn.ERR_UNSUPPORTED),
+    (dict(causal=1, S_q=300, S_k=100), attn.ERR_UNSUPPORTED),
+    (dict(q=P + 8), attn.ERR_MISALIGNED),
+    (dict(o=P + 2), attn.ERR_MISALIGNED),
+    (dict(lse=P + 2), attn.ERR_MISALIGNED),
+])
+def test_validation_rejects(kw, code):
+    assert chk(**kw) == code
+
+
+def test_split_plan():
+    # the decode shape splits its 32K keys; ordinary prefill does not
+    assert attn.num_splits(64, 32, 1, 32768, 128) > 1
+    assert attn.num_splits(2, 16, 8192, 8192, 128) == 1
+    assert attn.num_splits(1, 1, 128, 128, 128, 1) == 1
+    # requests are clamped to the number of key tiles and never leave a split empty
+    assert attn.num_splits(1, 1, 4, 100, 128, 16) == 2
+    assert attn.num_splits(1, 1, 4, 640, 128, 4) == 4
+    assert attn.workspace_size(1, 1, 4, 640, 128, 1) == 0
+    n = attn.num_splits(64, 32, 1, 32768, 128)
+    assert attn.workspace_size(64, 32, 1, 32768, 128) >= n * 64 * 32 * (128 + 1) * 4
