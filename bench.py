@@ -1,0 +1,244 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused attention forward pass on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extras] [--no-cpu-baseline]
+
+One step is one call of ``attn_fwd`` on the headline workload: bfloat16,
+B=2, H=16, S_q=S_k=8192, D=128, non-causal, inputs N(0,1) already resident in
+HBM. W untimed steps, then exactly K timed steps between two synchronisations.
+FLOPs per step: 4*B*H*S_q*S_k*D (halved for causal workloads).
+
+Printed: ONE JSON line with the headline throughput, the roofline of the
+kernel (its average launch duration from HIP events recorded on the stream it
+runs on, inside the timed region), the CPU oracle timed on a bounded sample,
+and (unless --no-extras) the other configured workloads as extra figures: the
+D=64 non-causal and D=128 causal sweeps over S = 512..16K, the D=256 causal 8K
+shape, the S_q=1 / S_k=32K decode shape with its key-range split, and the FP8
+pipeline (Hadamard + block quantization, per-tensor V quantization, FP8
+attention) with its error against exact attention.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from exact_attention_47_amd import attn, inputs  # noqa: E402
+
+METRIC = "fwd attention TFLOPS & % of MFMA peak, bf16/fp8, hdim 128, seqlen 512–16K"
+PEAK_BF16 = 2500.0      # TFLOP/s, dense bf16/fp16 MFMA
+PEAK_FP8 = 5000.0       # TFLOP/s, dense fp8 MFMA
+PEAK_HBM = 8000.0       # GB/s
+
+
+def flops(B, H, S_q, S_k, D, causal):
+    f = 4.0 * B * H * S_q * S_k * D
+    return f / 2 if causal else f
+
+
+def time_launches(fn, steps, warmup):
+    """Average milliseconds per call of fn (events on the current stream), after warmup."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    for i in range(steps):
+        starts[i].record()
+        fn()
+        ends[i].record()
+    torch.cuda.synchronize()
+    per = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    return sum(per) / len(per), min(per)
+
+
+def bf16_point(B, H, S_q, S_k, D, causal, steps=10, warmup=3, seed=0):
+    q, k, v = inputs.qkv(B, H, S_q, S_k, D, seed=seed, dtype=torch.bfloat16, device="cuda")
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, S_q), dtype=torch.float32, device="cuda")
+    scale = 1 / math.sqrt(D)
+    ms, ms_min = time_launches(lambda: attn.fwd(q, k, v, causal, scale, out=o, lse=lse), steps, warmup)
+    fl = flops(B, H, S_q, S_k, D, causal)
+    res = {"B": B, "H": H, "S_q": S_q, "S_k": S_k, "D": D, "causal": causal, "ms": round(ms, 4),
+           "tflops": round(fl / ms / 1e9, 1), "pct_peak": round(100 * fl / ms / 1e9 / PEAK_BF16, 1)}
+    del q, k, v, o, lse
+    torch.cuda.empty_cache()
+    return res
+
+
+def decode_point(steps=10, warmup=3):
+    B, H, S_k, D = 64, 32, 32768, 128
+    q, k, v = inputs.qkv(B, H, 1, S_k, D, seed=0, dtype=torch.bfloat16, device="cuda")
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, 1), dtype=torch.float32, device="cuda")
+    n = attn.num_splits(B, H, 1, S_k, D)
+    ws = torch.empty(max(1, attn.workspace_size(B, H, 1, S_k, D)), dtype=torch.uint8, device="cuda")
+    ms, _ = time_launches(lambda: attn.fwd(q, k, v, False, 1 / math.sqrt(D), out=o, lse=lse,
+                                           num_splits=0, workspace=ws), steps, warmup)
+    bytes_ = 2.0 * B * H * S_k * D * 2 + 2 * B * H * D * 2 + B * H * 4
+    res = {"B": B, "H": H, "S_q": 1, "S_k": S_k, "D": D, "n_split": n, "ms": round(ms, 4),
+           "gbps": round(bytes_ / ms / 1e6, 1), "pct_hbm_peak": round(100 * bytes_ / ms / 1e6 / PEAK_HBM, 1),
+           "tflops": round(flops(B, H, 1, S_k, D, False) / ms / 1e9, 2)}
+    del q, k, v, o, lse, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+def fp8_point(steps=10, warmup=3):
+    """FP8 pipeline on the outlier workload: B=2, H=16, S=8K, D=128, non-causal."""
+    B, H, S, D = 2, 16, 8192, 128
+    try:
+        q, k, v = inputs.qkv(B, H, S, S, D, seed=0, dtype=torch.bfloat16, device="cuda", outliers=True)
+        sg = inputs.signs(D, 0).cuda()
+        scale = 1 / math.sqrt(D)
+        q8, qs = attn.hadamard_quant(q, sg)
+        k8, ks = attn.hadamard_quant(k, sg)
+        v8, vs = attn.quant_per_tensor(v, transposed=True)
+        o, lse = attn.fwd_fp8(q8, k8, v8, qs, ks, vs, False, scale, v_transposed=True)
+    except attn.AttnError as e:
+        return {"status": f"not available: {e}"}
+    pre_ms, _ = time_launches(lambda: attn.hadamard_quant(q, sg), steps, warmup)
+    vq_ms, _ = time_launches(lambda: attn.quant_per_tensor(v, transposed=True), steps, warmup)
+    att_ms, _ = time_launches(lambda: attn.fwd_fp8(q8, k8, v8, qs, ks, vs, False, scale, v_transposed=True,
+                                                   out=o, lse=lse), steps, warmup)
+    fl = flops(B, H, S, S, D, False)
+    pre_bytes = B * H * S * D * (2 + 1) + B * H * (S // 64) * 4
+    vq_bytes = B * H * S * D * (2 + 2 + 1)
+    e2e = 2 * pre_ms + vq_ms + att_ms
+    res = {"B": B, "H": H, "S": S, "D": D, "attn_ms": round(att_ms, 4),
+           "attn_tflops": round(fl / att_ms / 1e9, 1), "attn_pct_fp8_peak": round(100 * fl / att_ms / 1e9 / PEAK_FP8, 1),
+           "hadamard_quant_ms": round(pre_ms, 4), "hadamard_quant_gbps": round(pre_bytes / pre_ms / 1e6, 1),
+           "v_quant_ms": round(vq_ms, 4), "v_quant_gbps": round(vq_bytes / vq_ms / 1e6, 1),
+           "pipeline_ms": round(e2e, 4), "pipeline_tflops": round(fl / e2e / 1e9, 1)}
+    del q, k, v, q8, k8, v8, o, lse
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(B, H, S, D, causal, heads=2):
+    """The CPU oracle (fp64, as it stands) on a bounded sample of the workload."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    q, k, v = inputs.qkv(1, heads, S, S, D, seed=0, dtype=torch.bfloat16)
+    q, k, v = (x.float().numpy().astype(np.float64) for x in (q, k, v))
+    t = time.perf_counter()
+    oracle.attention(q, k, v, causal, 1 / math.sqrt(D))
+    dt = time.perf_counter() - t
+    fl = flops(1, heads, S, S, D, causal)
+    return {"value": round(fl / dt / 1e12, 5), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"oracle.attention (float64, explicit score matrix) on {heads} heads of the workload "
+                      f"({S}x{S} scores, D={D}): {dt:.2f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-extras", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="instead of the bench, run K plain device-to-device copies of this many bytes "
+                         "(reference for scaling memory-traffic counters)")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (each (b, h) is independent; "
+              "sharding would split B*H across GPUs with no communication). Run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    if args.copy_bytes > 0:
+        a = torch.empty(args.copy_bytes, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        ms, _ = time_launches(lambda: b.copy_(a), args.steps, args.warmup)
+        print(json.dumps({"copy_bytes": args.copy_bytes, "ms": round(ms, 4),
+                          "gbps_read_plus_write": round(2 * args.copy_bytes / ms / 1e6, 1)}), flush=True)
+        return
+    attn.load()
+
+    B, H, S, D, causal = 2, 16, 8192, 128, False
+    q, k, v = inputs.qkv(B, H, S, S, D, seed=0, dtype=torch.bfloat16, device="cuda")
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, S), dtype=torch.float32, device="cuda")
+    scale = 1 / math.sqrt(D)
+
+    def step():
+        attn.fwd(q, k, v, causal, scale, out=o, lse=lse)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s, e in ev:
+        s.record(stream)
+        step()
+        e.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern_ms = sum(s.elapsed_time(e) for s, e in ev) / len(ev)
+    ms_per_step = wall * 1e3 / args.steps
+    fl = flops(B, H, S, S, D, causal)
+    value = fl / (ms_per_step * 1e-3) / 1e12
+    achieved = fl / (kern_ms * 1e-3) / 1e12
+    del q, k, v, o, lse
+    torch.cuda.empty_cache()
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: Q, K, V iid N(0,1) rounded to bfloat16, seed 0, resident in HBM",
+        "config": {"workload": "attention forward, bf16, non-causal, B=2 H=16 S_q=S_k=8192 D=128 "
+                               "(hdim 128, seqlen 8K)", "global_batch": B, "seq_len": S, "heads": H,
+                   "head_dim": D, "causal": causal, "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16, 4), "traffic": None,
+                     "kernel": "fwd_mfma_kernel<bf16, D=128, QB=2, non-causal>",
+                     "kernel_ms": round(kern_ms, 4)},
+        "context": {"pages_h100_fa3_fp16_fwd_hdim128_seqlen8k_tflops": "640-660 (H100, not this machine)"},
+    }
+    if not args.no_extras:
+        extras = {}
+        extras["noncausal_d64_sweep"] = [bf16_point(16384 // s, 32, s, s, 64, False) for s in
+                                         (512, 1024, 2048, 4096, 8192, 16384)]
+        extras["causal_d128_sweep"] = [bf16_point(16384 // s, 16, s, s, 128, True) for s in
+                                       (512, 1024, 2048, 4096, 8192, 16384)]
+        extras["causal_d256_8k"] = bf16_point(2, 8, 8192, 8192, 256, True)
+        extras["decode_32k"] = decode_point()
+        extras["fp8_pipeline_8k"] = fp8_point()
+        out["extras"] = extras
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(B, H, S, D, causal)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -23,9 +23,8 @@ void say(const char* what, int status) {
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
-int key_tile(int dtype) { return dtype == ATTN_F32 ? attn::f32_keys_per_tile() : attn::mfma_keys_per_tile(); }
-int rows_per_block(int dtype, int D) {
-  return dtype == ATTN_F32 ? attn::f32_rows_per_block() : attn::mfma_rows_per_block(D);
+int key_tile(int dtype, int D) {
+  return dtype == ATTN_F32 ? attn::f32_keys_per_tile() : attn::mfma_keys_per_tile(D);
 }
 
 // Split plan: effective split count and keys per split (a multiple of the key tile).
@@ -35,8 +34,8 @@ struct Plan {
 };
 
 Plan plan_splits(int dtype, int B, int H, int S_q, int S_k, int D, int req) {
-  (void)B; (void)H; (void)D;
-  const int tile = key_tile(dtype);
+  (void)B; (void)H;
+  const int tile = key_tile(dtype, D);
   const int n_tiles = (S_k + tile - 1) / tile;
   int n = 1;
   if (req > 1) {

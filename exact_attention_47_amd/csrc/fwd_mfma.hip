@@ -3,38 +3,48 @@
 // What is computed: O = softmax(scale * Q K^T [+ causal mask]) V and the row
 // logsumexp, block by block with online softmax rescaling, so the score matrix
 // never reaches HBM ([NL] "FlashAttention en FlashAttention-2"; [GN]
-// "Rueckblick auf den FlashAttention-Ansatz"). The pages' Hopper schedule
-// (asynchronous GEMMs overlapped with softmax, loads in the shadow of compute;
-// [GN] "Ueberlappung von GEMM und Softmax durch Asynchronitaet", [NL]
-// "2. Minimalisatie van geheugenoperaties") is mapped onto CDNA4 as follows.
+// "Rueckblick auf den FlashAttention-Ansatz").
 //
-// Work split: one workgroup of 4 waves per (b, h, block of BM query rows);
-// each wave owns RPW = 32*QB query rows for the whole key loop. Keys are
-// processed in tiles of BN = 64, staged in LDS with two buffers so that the
-// global loads of tile t+1 are in flight while tile t is computed.
+// CDNA4 mapping of the pages' Hopper schedule:
 //
-// Both GEMMs are written transposed so that one lane owns one query row:
-//   S^T = K Q^T   (v_mfma_f32_32x32x16: A = K tile rows from LDS, B = Q^T
-//                  held in VGPRs for the whole loop); the accumulator lane
-//                  (h, n) holds 16 keys of query n, so the row max and row
-//                  sum need no cross-lane work except one exchange with the
-//                  lane 32 away.
-//   O^T = V^T P^T (A = V^T read from LDS with ds_read_b64_tr_b16, which
-//                  transposes 4x16 blocks in flight; B = P^T, which is the
-//                  S^T accumulator itself after exp2 and a conversion: the
-//                  accumulator element order already matches the B operand's
-//                  k order, given the matching choice of keys for V^T).
-// The softmax works in base 2 with the scale folded in: t = s * scale*log2(e),
-// p = 2^(t - m). The running reference m is only moved when a row's maximum
-// exceeds it by more than TAU (p stays <= 2^TAU), which skips most O
-// rescales and is still exact: the final O / l and the LSE use the same m.
+// * Work split. One workgroup of 8 waves per (b, h, 256 query rows); each wave
+//   owns 32 query rows for the whole key loop and holds Q^T in registers. Keys
+//   are processed in tiles of BN.
 //
-// LDS layout (per buffer): K tile [BN][D] with a row stride of 2*D + 16
-// bytes, V tile [BN][D] with a stride of 2*D + 32 bytes. With 32 four-byte
-// banks, the K reads (8 lanes per pass, 8 consecutive rows, same column) and
-// the transposed V reads (16 lanes per pass, 4 consecutive rows x 32 bytes)
-// both touch distinct banks, and every address is a per-lane base plus a
-// compile-time offset.
+// * Ping-pong ([GN] "Pingpong-Scheduling zwischen Warpgroups"). Waves w and
+//   w+4 share a SIMD. Waves 0-3 (group 0) and 4-7 (group 1) run the same
+//   loop half a step apart: while one group issues its matrix instructions
+//   (P V of the previous tile, then Q K^T of the current one) the other group
+//   runs the softmax of its latest tile on the vector ALU, and at each
+//   workgroup barrier they swap. The group issuing matrix instructions raises
+//   its wave priority so the MFMA pipe is fed first.
+//
+// * Loads in the shadow of compute ([NL] "2. Minimalisatie van
+//   geheugenoperaties"). Stage t of a two-buffer LDS ring holds K(t) and
+//   V(t-1): exactly the operands of the matrix phase that reads it. Stage t+1
+//   is fetched with global_load_lds_dwordx4 (global memory straight into LDS,
+//   no registers) at the start of the step that reads stage t, and waited
+//   for just before the step's closing barrier.
+//
+// * Both GEMMs are transposed so that one lane owns one query row:
+//   S^T = K Q^T with v_mfma_f32_32x32x16 (A = K rows from LDS, B = Q^T from
+//   VGPRs): lane (h, n) holds 16 keys of query n, so row max and row sum need
+//   one exchange with lane n+32 only. O^T = V^T P^T (A = V^T read with
+//   ds_read_b64_tr_b16, which transposes in flight; B = P^T, which is the S^T
+//   accumulator after exp2 and conversion, already in the B operand's k order
+//   given the matching choice of keys for V^T).
+//
+// * Softmax in base 2 with the scale folded in: p = 2^(s * c - m), c =
+//   scale * log2(e). The reference m moves only when a row's maximum exceeds
+//   it by more than TAU (p <= 2^TAU): rescales of O become rare, and the
+//   result is still exact because the final O / l and LSE use the same m.
+//
+// * LDS layout. Tiles are stored unpadded ([BN][D]) with a 16-byte-chunk XOR
+//   swizzle that depends on the row, so that the K reads (16 lanes per LDS
+//   cycle: 16 rows, one chunk each) and the transposed V reads (32 lanes per
+//   cycle: 4 rows x 64 bytes) each touch all 64 banks once. The direct loads
+//   write 1 KiB per wave instruction, lane i at byte 16*i; each lane fetches
+//   the global chunk that the swizzle places there.
 #include "common.h"
 #include "kernels.h"
 
@@ -56,43 +66,48 @@ template <> struct Mma<_Float16> {
   static __device__ __forceinline__ frag cvt(v8f x) { return __builtin_convertvector(x, v8f16); }
 };
 
-template <int D, int QB>
+template <int D, int BN_>
 struct FwdCfg {
-  static constexpr int NW = 4;                  // waves per workgroup
-  static constexpr int RPW = 32 * QB;           // query rows per wave
-  static constexpr int BM = NW * RPW;           // query rows per workgroup
-  static constexpr int BN = 64;                 // keys per tile
+  static constexpr int NW = 8;                  // waves per workgroup (two groups of 4)
+  static constexpr int NT = NW * 64;
+  static constexpr int BM = NW * 32;            // query rows per workgroup
+  static constexpr int BN = BN_;                // keys per tile
   static constexpr int KB = BN / 32;            // 32-key blocks per tile
   static constexpr int DS = D / 16;             // k-steps of the S^T product
   static constexpr int DB = D / 32;             // 32-wide column blocks of O^T
-  static constexpr int CH = D / 8;              // 16-byte chunks per row
-  static constexpr int KS = 2 * D + 16;         // K row stride in LDS (bytes)
-  static constexpr int VS = 2 * D + 32;         // V row stride in LDS (bytes)
-  static constexpr int KT = BN * KS;            // K tile bytes
-  static constexpr int VT = BN * VS;            // V tile bytes
-  static constexpr int STAGE = KT + VT;
+  static constexpr int RB = 2 * D;              // bytes per K/V row
+  static constexpr int TILE = BN * RB;          // bytes per K or V tile
+  static constexpr int STAGE = 2 * TILE;        // K(t) then V(t-1)
   static constexpr int LDS = 2 * STAGE;
-  static constexpr int NCH = BN * CH / 256;     // 16-byte chunks per thread per tile
+  static constexpr int NI = TILE / (NT * 16);   // direct-load instructions per thread per tile
+  static constexpr int RPI = 1024 / RB;         // rows written by one wave instruction
+  static_assert(TILE % (NT * 16) == 0, "tile must split evenly into 1 KiB wave loads");
 };
 
-constexpr float kTau = 8.0f;   // lazy-rescale threshold, log2 domain
+// Row-dependent 16-byte-chunk XOR swizzles of the K and V tiles.
+template <int D> __device__ __forceinline__ int k_swz(int r) { return D == 64 ? (r >> 1) & 7 : r & 15; }
+template <int D> __device__ __forceinline__ int v_swz(int r) { return D == 64 ? 4 * ((r >> 1) & 1) : 4 * (r & 3); }
 
-template <typename T, int D, int QB, bool CAUSAL, bool SPLIT>
-__global__ void __launch_bounds__(256)
-__attribute__((amdgpu_waves_per_eu(1, 1)))
+constexpr float kTau = 8.0f;   // lazy-rescale threshold, log2 domain
+constexpr int kVmcnt0 = 0x0070 | 0x0F00;   // s_waitcnt vmcnt(0), other counters unconstrained
+
+template <typename T, int D, int BN, bool CAUSAL, bool SPLIT>
+__global__ void __launch_bounds__(512)
+__attribute__((amdgpu_waves_per_eu(2, 2)))
 fwd_mfma_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
                 T* __restrict__ O, float* __restrict__ LSE,
                 float* __restrict__ Opart, float* __restrict__ Lpart,
                 int BH, int S_q, int S_k, int n_qt, int n_split, int keys_per_split, float c)
 {
-  using C = FwdCfg<D, QB>;
+  using C = FwdCfg<D, BN>;
   using M = Mma<T>;
   typedef typename M::frag frag;
-  __shared__ __attribute__((aligned(16))) char lds[C::LDS];
+  __shared__ __attribute__((aligned(1024))) char lds[C::LDS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2;       // ping-pong group
   const int hh = lane >> 5;        // lane half
   const int nn = lane & 31;        // query column owned by this lane
 
@@ -106,7 +121,7 @@ fwd_mfma_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
   if (CAUSAL) qt = n_qt - 1 - qt;  // heaviest query tiles first
 
   const int q0 = qt * C::BM;
-  const int wr0 = q0 + wave * C::RPW;          // first row of this wave
+  const int wr0 = q0 + wave * 32;              // first row of this wave
   const int diag = S_k - S_q;                  // causal: key j allowed iff j <= i + diag
   int k_lo = 0, k_hi = S_k;
   if (SPLIT) {
@@ -124,267 +139,307 @@ fwd_mfma_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
   const T* Vh = V + koff;
 
   // ---- Q^T fragments (B operand of S^T), kept in registers
-  frag qf[QB][C::DS];
-#pragma unroll
-  for (int qb = 0; qb < QB; qb++) {
-    const int q = wr0 + qb * 32 + nn;
+  frag qf[C::DS];
+  {
+    const int q = wr0 + nn;
 #pragma unroll
     for (int ds = 0; ds < C::DS; ds++) {
       if (q < S_q) {
-        qf[qb][ds] = *(const frag*)(Qh + (size_t)q * D + ds * 16 + 8 * hh);
+        qf[ds] = *(const frag*)(Qh + (size_t)q * D + ds * 16 + 8 * hh);
       } else {
 #pragma unroll
-        for (int e = 0; e < 8; e++) qf[qb][ds][e] = (T)0.0f;
+        for (int e = 0; e < 8; e++) qf[ds][e] = (T)0.0f;
       }
     }
   }
 
-  // ---- global -> register staging of one K/V tile
-  uint4 kst[C::NCH], vst[C::NCH];
-  auto gload = [&](int key0) {
+  // ---- direct global -> LDS loads, issued by the 256 threads of group 0:
+  // stage s = K(s) (if s < n_tiles) and V(s-1) (if s >= 1) into buffer s & 1.
+  // Each wave instruction fills 1 KiB (RPI rows); lane i lands at byte 16*i
+  // and fetches the logical chunk the swizzle stores there. Rows past the key
+  // range read the last valid key row (their scores are masked).
+  auto issue_stage = [&](int s) {
+    char* base = lds + (s & 1) * C::STAGE;
+    const int rsub = (lane * 16) / C::RB;           // row within the wave instruction
+    const int u = ((lane * 16) % C::RB) / 16;       // physical chunk within the row
 #pragma unroll
-    for (int i = 0; i < C::NCH; i++) {
-      const int id = i * 256 + tid;
-      const int r = id / C::CH, cc = id % C::CH;
-      const int key = key0 + r;
-      if (key < k_hi) {
-        kst[i] = *(const uint4*)(Kh + (size_t)key * D + cc * 8);
-        vst[i] = *(const uint4*)(Vh + (size_t)key * D + cc * 8);
-      } else {
-        kst[i] = make_uint4(0, 0, 0, 0);
-        vst[i] = make_uint4(0, 0, 0, 0);
+    for (int kv = 0; kv < 2; kv++) {
+      const int t = s - kv;                          // K(s) then V(s-1)
+      if (t < 0 || t >= n_tiles) continue;
+      const int key0 = k_lo + t * C::BN;
+      const T* src0 = kv == 0 ? Kh : Vh;
+#pragma unroll
+      for (int i = 0; i < 2 * C::NI; i++) {
+        const int blk = i * 4 + wave;                // 1 KiB block of the tile
+        const int r = blk * C::RPI + rsub;
+        const int cchunk = u ^ (kv == 0 ? k_swz<D>(r) : v_swz<D>(r));
+        const int key = min(key0 + r, S_k - 1);
+        const T* src = src0 + (size_t)key * D + cchunk * 8;
+        __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)src,
+                                         (void __attribute__((address_space(3)))*)(base + kv * C::TILE + blk * 1024),
+                                         16, 0, 0);
       }
     }
   };
-  auto swrite = [&](int buf) {
-    char* kb = lds + buf * C::STAGE;
-    char* vb = kb + C::KT;
-#pragma unroll
-    for (int i = 0; i < C::NCH; i++) {
-      const int id = i * 256 + tid;
-      const int r = id / C::CH, cc = id % C::CH;
-      *(uint4*)(kb + r * C::KS + cc * 16) = kst[i];
-      *(uint4*)(vb + r * C::VS + cc * 16) = vst[i];
-    }
-  };
 
-  // per-lane LDS bases
-  const int kbase = nn * C::KS + hh * 16;
+  // ---- per-lane LDS read offsets (swizzle folded in)
+  // The XOR only reaches the low 3 (K) / 2 (V) bits of the chunk index, so
+  // the offsets repeat every 8 k-steps / 4 column blocks up to a constant.
+  constexpr int NKR = C::DS < 8 ? C::DS : 8;
+  constexpr int NVR = C::DB < 4 ? C::DB : 4;
+  const int xk = k_swz<D>(nn);                 // K row = kb*32 + nn: swizzle depends on nn only
+  int k_rd[NKR];
+#pragma unroll
+  for (int ds = 0; ds < NKR; ds++) k_rd[ds] = nn * C::RB + (((2 * ds + hh) ^ xk) * 16);
   const int g = lane >> 4, jj = lane & 15;
-  const int vbase = (4 * hh + (jj >> 2)) * C::VS + 32 * (g & 1) + 8 * (jj & 3);
+  const int vrow = 4 * hh + (jj >> 2);         // V row = vrow + kb*32 + 16*ks + 8*part
+  const int xv = v_swz<D>(vrow);               // depends on vrow's low bits only
+  int v_rd[NVR];
+#pragma unroll
+  for (int db = 0; db < NVR; db++)
+    v_rd[db] = vrow * C::RB + (((4 * db + 2 * (g & 1) + ((jj & 3) >> 1)) ^ xv) * 16) + 8 * (jj & 1);
 
-  v16f o[QB][C::DB];
+  v16f o[C::DB];
 #pragma unroll
-  for (int qb = 0; qb < QB; qb++)
+  for (int db = 0; db < C::DB; db++)
 #pragma unroll
-    for (int db = 0; db < C::DB; db++)
-#pragma unroll
-      for (int e = 0; e < 16; e++) o[qb][db][e] = 0.0f;
-  float m[QB], l[QB];
-#pragma unroll
-  for (int qb = 0; qb < QB; qb++) { m[qb] = kNegInf; l[qb] = 0.0f; }
+    for (int e = 0; e < 16; e++) o[db][e] = 0.0f;
+  v16f s[C::KB];
+  frag pf[C::KB][2];
+  float m = kNegInf, l = 0.0f;
 
-  if (n_tiles > 0) {
-    gload(k_lo);
-    swrite(0);
-  }
-  __syncthreads();
+  // causal: tiles that lie wholly after this wave's last row are skipped
+  auto tile_active = [&](int t) { return !CAUSAL || k_lo + t * C::BN <= wr0 + 31 + diag; };
 
-  for (int t = 0; t < n_tiles; t++) {
-    const int key0 = k_lo + t * C::BN;
-    if (t + 1 < n_tiles) gload(key0 + C::BN);
-    const char* kl = lds + (t & 1) * C::STAGE;
-    const char* vl = kl + C::KT;
-
-    // causal: this wave's rows may all precede the tile
-    const bool active = !CAUSAL || key0 <= wr0 + C::RPW - 1 + diag;
-    if (active) {
-      // ---- S^T = K Q^T
-      v16f s[C::KB][QB];
+  // matrix phase: O^T += V(t-1)^T P(t-1)^T, then S(t)^T = K(t) Q^T.
+  // Each product is a list of steps (one A fragment from LDS, one MFMA); the
+  // fragment of step j+LA is loaded while step j multiplies, and a scheduling
+  // barrier after every step keeps the compiler from hoisting further loads
+  // (which would cost registers the two waves per SIMD do not have).
+  constexpr int LA = 3;
+  constexpr int NPV = C::KB * 2 * C::DB;      // steps of O^T += V^T P^T
+  constexpr int NSK = C::DS * C::KB;          // steps of S^T = K Q^T
+  auto gemm_phase = [&](int t) {
+    const char* st = lds + (t & 1) * C::STAGE;
+    if (t >= 1 && tile_active(t - 1)) {
+      const char* vl = st + C::TILE;
+      auto load = [&](int j) {
+        const int kb = j / (2 * C::DB), ks = (j / C::DB) % 2, db = j % C::DB;
+        const int off = (kb * 32 + 16 * ks) * C::RB;
+        const char* va = vl + v_rd[db % NVR] + (db / NVR) * 256 + off;
+        v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)va);
+        v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(va + 8 * C::RB));
+        return __builtin_bit_cast(frag, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      };
+      frag ring[LA + 1];
 #pragma unroll
-      for (int kb = 0; kb < C::KB; kb++)
+      for (int j = 0; j < LA; j++) ring[j] = load(j);
 #pragma unroll
-        for (int qb = 0; qb < QB; qb++)
-#pragma unroll
-          for (int e = 0; e < 16; e++) s[kb][qb][e] = 0.0f;
-#pragma unroll
-      for (int ds = 0; ds < C::DS; ds++) {
-#pragma unroll
-        for (int kb = 0; kb < C::KB; kb++) {
-          const frag a = *(const frag*)(kl + kbase + kb * 32 * C::KS + ds * 32);
-#pragma unroll
-          for (int qb = 0; qb < QB; qb++) s[kb][qb] = M::mma(a, qf[qb][ds], s[kb][qb]);
-        }
+      for (int j = 0; j < NPV; j++) {
+        if (j + LA < NPV) ring[(j + LA) % (LA + 1)] = load(j + LA);
+        const int kb = j / (2 * C::DB), ks = (j / C::DB) % 2, db = j % C::DB;
+        o[db] = M::mma(ring[j % (LA + 1)], pf[kb][ks], o[db]);
+        __builtin_amdgcn_sched_barrier(0);
       }
-
-      // ---- mask: keys past the range end, and the causal diagonal
-      const bool need_mask = (key0 + C::BN > k_hi) || (CAUSAL && key0 + C::BN - 1 > wr0 + diag);
-      if (need_mask) {
-#pragma unroll
-        for (int kb = 0; kb < C::KB; kb++)
-#pragma unroll
-          for (int qb = 0; qb < QB; qb++) {
-            const int q = wr0 + qb * 32 + nn;
-#pragma unroll
-            for (int i = 0; i < 4; i++)
-#pragma unroll
-              for (int j = 0; j < 4; j++) {
-                const int key = key0 + kb * 32 + 8 * i + 4 * hh + j;
-                const bool ok = key < k_hi && (!CAUSAL || key <= q + diag);
-                if (!ok) s[kb][qb][4 * i + j] = kNegInf;
-              }
-          }
-      }
-
-      // ---- online softmax (base 2, scale folded into c)
-      float mx[QB];
-      bool grow = false;
-#pragma unroll
-      for (int qb = 0; qb < QB; qb++) {
-        float x = kNegInf;
-#pragma unroll
-        for (int kb = 0; kb < C::KB; kb++)
-#pragma unroll
-          for (int e = 0; e < 16; e++) x = fmaxf(x, s[kb][qb][e]);
-        x = pair_max(x) * c;
-        mx[qb] = x;
-        grow |= x > m[qb] + kTau;
-      }
-      if (__any(grow)) {
-#pragma unroll
-        for (int qb = 0; qb < QB; qb++) {
-          const float mnew = fmaxf(m[qb], mx[qb]);
-          const float ref = mnew == kNegInf ? 0.0f : mnew;
-          const float alpha = fast_exp2(m[qb] - ref);   // 0 when m was -inf
-          m[qb] = mnew;
-          l[qb] *= alpha;
-#pragma unroll
-          for (int db = 0; db < C::DB; db++)
-#pragma unroll
-            for (int e = 0; e < 16; e++) o[qb][db][e] *= alpha;
-        }
-      }
-#pragma unroll
-      for (int qb = 0; qb < QB; qb++) {
-        const float ref = m[qb] == kNegInf ? 0.0f : m[qb];
-        float ls = 0.0f;
-#pragma unroll
-        for (int kb = 0; kb < C::KB; kb++)
-#pragma unroll
-          for (int e = 0; e < 16; e++) {
-            const float p = fast_exp2(__builtin_fmaf(s[kb][qb][e], c, -ref));
-            s[kb][qb][e] = p;
-            ls += p;
-          }
-        l[qb] += ls;
-      }
-
-      // ---- O^T += V^T P^T
-#pragma unroll
-      for (int kb = 0; kb < C::KB; kb++)
-#pragma unroll
-        for (int ks = 0; ks < 2; ks++) {
-          frag pf[QB];
-#pragma unroll
-          for (int qb = 0; qb < QB; qb++) {
-            v8f x;
-#pragma unroll
-            for (int e = 0; e < 8; e++) x[e] = s[kb][qb][8 * ks + e];
-            pf[qb] = M::cvt(x);
-          }
-#pragma unroll
-          for (int db = 0; db < C::DB; db++) {
-            const int off = (kb * 32 + 16 * ks) * C::VS + db * 64;
-            v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vl + vbase + off));
-            v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vl + vbase + off + 8 * C::VS));
-            v8i16 a16 = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-            const frag a = __builtin_bit_cast(frag, a16);
-#pragma unroll
-            for (int qb = 0; qb < QB; qb++) o[qb][db] = M::mma(a, pf[qb], o[qb][db]);
-          }
-        }
     }
+    if (t < n_tiles && tile_active(t)) {
+      auto load = [&](int j) {
+        const int ds = j / C::KB, kb = j % C::KB;
+        return *(const frag*)(st + k_rd[ds % NKR] + (ds / NKR) * 256 + kb * 32 * C::RB);
+      };
+      frag ring[LA + 1];
+#pragma unroll
+      for (int j = 0; j < LA; j++) ring[j] = load(j);
+#pragma unroll
+      for (int j = 0; j < NSK; j++) {
+        if (j + LA < NSK) ring[(j + LA) % (LA + 1)] = load(j + LA);
+        const int ds = j / C::KB, kb = j % C::KB;
+        if (ds == 0) {
+          const v16f zero = {};
+          s[kb] = M::mma(ring[j % (LA + 1)], qf[ds], zero);
+        } else {
+          s[kb] = M::mma(ring[j % (LA + 1)], qf[ds], s[kb]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
 
-    if (t + 1 < n_tiles) swrite((t + 1) & 1);
+  // vector phase: mask, online softmax of S(t), P(t) -> matrix-operand fragments
+  auto softmax_phase = [&](int t) {
+    if (t < 0 || t >= n_tiles || !tile_active(t)) return;
+    const int key0 = k_lo + t * C::BN;
+    const bool need_mask = (key0 + C::BN > k_hi) || (CAUSAL && key0 + C::BN - 1 > wr0 + diag);
+    if (need_mask) {
+      const int q = wr0 + nn;
+#pragma unroll
+      for (int kb = 0; kb < C::KB; kb++)
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+#pragma unroll
+          for (int j = 0; j < 4; j++) {
+            const int key = key0 + kb * 32 + 8 * i + 4 * hh + j;
+            const bool ok = key < k_hi && (!CAUSAL || key <= q + diag);
+            if (!ok) s[kb][4 * i + j] = kNegInf;
+          }
+    }
+    float x = kNegInf;
+#pragma unroll
+    for (int kb = 0; kb < C::KB; kb++)
+#pragma unroll
+      for (int e = 0; e < 16; e++) x = fmaxf(x, s[kb][e]);
+    x = pair_max(x) * c;
+    if (__any(x > m + kTau)) {
+      const float mnew = fmaxf(m, x);
+      const float ref = mnew == kNegInf ? 0.0f : mnew;
+      const float alpha = fast_exp2(m - ref);   // 0 when m was -inf
+      m = mnew;
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < C::DB; db++)
+#pragma unroll
+        for (int e = 0; e < 16; e++) o[db][e] *= alpha;
+    }
+    const float ref = m == kNegInf ? 0.0f : m;
+    float ls = 0.0f;
+#pragma unroll
+    for (int kb = 0; kb < C::KB; kb++)
+#pragma unroll
+      for (int ks = 0; ks < 2; ks++) {
+        v8f pv;
+#pragma unroll
+        for (int e = 0; e < 8; e++) {
+          const float p = fast_exp2(__builtin_fmaf(s[kb][8 * ks + e], c, -ref));
+          pv[e] = p;
+          ls += p;
+        }
+        pf[kb][ks] = M::cvt(pv);
+      }
+    l += ls;
+  };
+
+  // Both groups run the same body, gemm(j) | barrier | softmax(j) | barrier;
+  // group 1 starts one barrier later and group 0 ends one barrier later, so
+  // group 1's matrix phase overlaps group 0's softmax and vice versa. Group 0
+  // fetches stage j+1 at the start of its softmax phase j and waits for it
+  // before that phase's closing barrier: both groups have finished reading
+  // stage j-1 (the buffer it overwrites) by then, stage j+1 is complete
+  // before either group reads it, and no LDS read is ever issued while a
+  // direct load is in flight (so the compiler adds no waits of its own).
+  // Inside the loop the barriers are bare s_barrier: the only memory that
+  // must be settled at a barrier is the staged tile, waited for explicitly.
+  auto barrier = [] {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+  };
+  if (n_tiles > 0) {
+    if (grp == 0) issue_stage(0);
+    __builtin_amdgcn_s_waitcnt(kVmcnt0);
     __syncthreads();
+    if (grp == 1) barrier();
+    for (int j = 0; j <= n_tiles; j++) {
+      __builtin_amdgcn_s_setprio(1);
+      gemm_phase(j);
+      __builtin_amdgcn_s_setprio(0);
+      barrier();
+      if (grp == 0) issue_stage(j + 1);
+      softmax_phase(j);
+      __builtin_amdgcn_s_waitcnt(kVmcnt0);
+      barrier();
+    }
+    if (grp == 0) barrier();
   }
 
   // ---- epilogue: normalise, logsumexp, store
+  const int q = wr0 + nn;
+  const float lt = pair_sum(l);
+  const bool has = m != kNegInf && lt > 0.0f;
+  const float inv = has ? 1.0f / lt : 0.0f;
+  const float lse = has ? (m + __builtin_log2f(lt)) * kLn2 : kNegInf;
+  if (q < S_q) {
+    if (!SPLIT) {
+      T* orow = O + qoff + (size_t)q * D;
 #pragma unroll
-  for (int qb = 0; qb < QB; qb++) {
-    const int q = wr0 + qb * 32 + nn;
-    const float lt = pair_sum(l[qb]);
-    const bool has = m[qb] != kNegInf && lt > 0.0f;
-    const float inv = has ? 1.0f / lt : 0.0f;
-    const float lse = has ? (m[qb] + __builtin_log2f(lt)) * kLn2 : kNegInf;
-    if (q < S_q) {
-      if (!SPLIT) {
-        T* orow = O + qoff + (size_t)q * D;
+      for (int db = 0; db < C::DB; db++)
 #pragma unroll
-        for (int db = 0; db < C::DB; db++)
+        for (int i = 0; i < 4; i++) {
+          typedef T v4t __attribute__((ext_vector_type(4)));
+          v4t w;
 #pragma unroll
-          for (int i = 0; i < 4; i++) {
-            typedef T v4t __attribute__((ext_vector_type(4)));
-            v4t w;
+          for (int j = 0; j < 4; j++) w[j] = (T)(o[db][4 * i + j] * inv);
+          *(v4t*)(orow + db * 32 + 8 * i + 4 * hh) = w;
+        }
+      if (hh == 0) LSE[(size_t)bh * S_q + q] = lse;
+    } else {
+      const size_t prow = ((size_t)split * BH + bh) * S_q + q;
+      float* orow = Opart + prow * D;
 #pragma unroll
-            for (int j = 0; j < 4; j++) w[j] = (T)(o[qb][db][4 * i + j] * inv);
-            *(v4t*)(orow + db * 32 + 8 * i + 4 * hh) = w;
-          }
-        if (hh == 0) LSE[(size_t)bh * S_q + q] = lse;
-      } else {
-        const size_t prow = ((size_t)split * BH + bh) * S_q + q;
-        float* orow = Opart + prow * D;
+      for (int db = 0; db < C::DB; db++)
 #pragma unroll
-        for (int db = 0; db < C::DB; db++)
-#pragma unroll
-          for (int i = 0; i < 4; i++) {
-            float4 w;
-            w.x = o[qb][db][4 * i + 0] * inv;
-            w.y = o[qb][db][4 * i + 1] * inv;
-            w.z = o[qb][db][4 * i + 2] * inv;
-            w.w = o[qb][db][4 * i + 3] * inv;
-            *(float4*)(orow + db * 32 + 8 * i + 4 * hh) = w;
-          }
-        if (hh == 0) Lpart[prow] = lse;
-      }
+        for (int i = 0; i < 4; i++) {
+          float4 w;
+          w.x = o[db][4 * i + 0] * inv;
+          w.y = o[db][4 * i + 1] * inv;
+          w.z = o[db][4 * i + 2] * inv;
+          w.w = o[db][4 * i + 3] * inv;
+          *(float4*)(orow + db * 32 + 8 * i + 4 * hh) = w;
+        }
+      if (hh == 0) Lpart[prow] = lse;
     }
   }
 }
 
 // ---------------------------------------------------------------- launchers
 
-template <typename T, int D, int QB, bool CAUSAL, bool SPLIT>
+// Keys per tile for each head dimension (LDS: 2 stages x (K + V) tiles).
+#ifndef FWD_D64_BN
+#define FWD_D64_BN 128
+#endif
+#ifndef FWD_D128_BN
+#define FWD_D128_BN 128
+#endif
+
+template <int D> struct Shape;
+template <> struct Shape<64> { static constexpr int BN = FWD_D64_BN; };
+template <> struct Shape<128> { static constexpr int BN = FWD_D128_BN; };
+
+template <typename T, int D, bool CAUSAL, bool SPLIT>
 static hipError_t launch_one(const FwdArgs& a, hipStream_t st) {
-  using C = FwdCfg<D, QB>;
+  using C = FwdCfg<D, Shape<D>::BN>;
   const int n_qt = (a.S_q + C::BM - 1) / C::BM;
   const int n_work = a.B * a.H * n_qt * a.n_split;
-  hipLaunchKernelGGL((fwd_mfma_kernel<T, D, QB, CAUSAL, SPLIT>), dim3(n_work), dim3(256), 0, st,
+  hipLaunchKernelGGL((fwd_mfma_kernel<T, D, Shape<D>::BN, CAUSAL, SPLIT>), dim3(n_work), dim3(C::NT), 0, st,
                      (const T*)a.q, (const T*)a.k, (const T*)a.v, (T*)a.o, a.lse, a.opart, a.lpart,
                      a.B * a.H, a.S_q, a.S_k, n_qt, a.n_split, a.keys_per_split, a.c);
   return hipGetLastError();
 }
 
-template <typename T, int D, int QB>
+template <typename T, int D>
 static hipError_t launch_d(const FwdArgs& a, hipStream_t st) {
   const bool split = a.n_split > 1;
-  if (a.causal) return split ? launch_one<T, D, QB, true, true>(a, st) : launch_one<T, D, QB, true, false>(a, st);
-  return split ? launch_one<T, D, QB, false, true>(a, st) : launch_one<T, D, QB, false, false>(a, st);
+  if (a.causal) return split ? launch_one<T, D, true, true>(a, st) : launch_one<T, D, true, false>(a, st);
+  return split ? launch_one<T, D, false, true>(a, st) : launch_one<T, D, false, false>(a, st);
 }
 
 template <typename T>
 static hipError_t launch_t(const FwdArgs& a, hipStream_t st) {
   switch (a.D) {
-    case 64: return launch_d<T, 64, 2>(a, st);
-    case 128: return launch_d<T, 128, 2>(a, st);
-    case 256: return launch_d<T, 256, 1>(a, st);
+    case 64: return launch_d<T, 64>(a, st);
+    case 128: return launch_d<T, 128>(a, st);
   }
   return hipErrorInvalidValue;
 }
 
-int mfma_rows_per_block(int D) { return D == 256 ? FwdCfg<256, 1>::BM : FwdCfg<128, 2>::BM; }
-int mfma_keys_per_tile() { return 64; }
+int mfma_keys_per_tile(int D) {
+  return D == 64 ? Shape<64>::BN : D == 128 ? Shape<128>::BN : d256_keys_per_tile();
+}
+int mfma_rows_per_block(int D) { (void)D; return 256; }
 
 hipError_t launch_fwd_mfma(const FwdArgs& a, hipStream_t st) {
+  if (a.D == 256) return launch_fwd_d256(a, st);
   if (a.dtype == 2) return launch_t<__bf16>(a, st);
   return launch_t<_Float16>(a, st);
 }

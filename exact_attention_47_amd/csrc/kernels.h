@@ -25,7 +25,11 @@ struct FwdArgs {
 // bf16 / fp16 matrix-core kernel
 hipError_t launch_fwd_mfma(const FwdArgs& a, hipStream_t st);
 int mfma_rows_per_block(int D);
-int mfma_keys_per_tile();
+int mfma_keys_per_tile(int D);
+
+// head dimension 256 (called through launch_fwd_mfma)
+hipError_t launch_fwd_d256(const FwdArgs& a, hipStream_t st);
+int d256_keys_per_tile();
 
 // float32 kernel
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t st);
