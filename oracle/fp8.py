@@ -23,7 +23,7 @@ reductie van kwantisatiefout"). Readings:
   stage order of ``oracle.hadamard.fwht`` (the transform is left unnormalised
   while choosing codes) and the block scale is then multiplied by
   r = fl32(1 / sqrt(D)) in float32, so that code * scale approximates
-  H diag(s) x / sqrt(D).
+  H diag(s) x / sqrt(D). An all-zero block keeps scale 1 (no factor r).
 
 All rounding decisions above are taken in float32, the precision of the
 quantize kernel, so the expected codes are unique.
@@ -80,11 +80,15 @@ def e4m3_encode(x) -> np.ndarray:
 
 
 def _block_quant_f32(u32: np.ndarray, block_rows: int):
-    """Quantize a float32 [B, H, S, D] array per (b, h, block of rows)."""
+    """Quantize a float32 [B, H, S, D] array per (b, h, block of rows).
+
+    Returns (codes, scales, nonzero) where nonzero flags the blocks with a > 0.
+    """
     b, h, s, d = u32.shape
     nblk = -(-s // block_rows)
     codes = np.zeros((b, h, s, d), dtype=np.uint8)
     scales = np.ones((b, h, nblk), dtype=np.float32)
+    nonzero = np.zeros((b, h, nblk), dtype=bool)
     for k in range(nblk):
         r0, r1 = k * block_rows, min(s, (k + 1) * block_rows)
         blk = u32[:, :, r0:r1, :]
@@ -96,13 +100,15 @@ def _block_quant_f32(u32: np.ndarray, block_rows: int):
         codes[:, :, r0:r1, :] = np.where(nz[:, :, None, None], e4m3_encode(y), 0)
         scales[:, :, k] = np.where(nz, (a_safe / np.float32(E4M3_MAX)).astype(np.float32),
                                    np.float32(1))
-    return codes, scales
+        nonzero[:, :, k] = nz
+    return codes, scales, nonzero
 
 
 def quantize_blocks(x, block_rows: int = 64):
     """Block quantization without a transform: (codes uint8 [B,H,S,D], scales f32 [B,H,nblk])."""
     x32 = np.asarray(x, dtype=np.float32)
-    return _block_quant_f32(x32, block_rows)
+    codes, scales, _ = _block_quant_f32(x32, block_rows)
+    return codes, scales
 
 
 def hadamard_quantize(x, signs, block_rows: int = 64):
@@ -115,9 +121,9 @@ def hadamard_quantize(x, signs, block_rows: int = 64):
     s = np.asarray(signs, dtype=np.float32)
     d = x32.shape[-1]
     u = fwht(x32 * s, dtype=np.float32)          # sign flips are exact
-    codes, scales = _block_quant_f32(u, block_rows)
+    codes, scales, nonzero = _block_quant_f32(u, block_rows)
     r = np.float32(1.0 / np.sqrt(np.float64(d)))
-    scales = (scales * r).astype(np.float32)
+    scales = np.where(nonzero, (scales * r).astype(np.float32), np.float32(1)).astype(np.float32)
     return codes, scales
 
 
