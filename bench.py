@@ -102,14 +102,14 @@ def fp8_point(steps=10, warmup=3):
         scale = 1 / math.sqrt(D)
         q8, qs = attn.hadamard_quant(q, sg)
         k8, ks = attn.hadamard_quant(k, sg)
-        v8, vs = attn.quant_per_tensor(v, transposed=True)
-        o, lse = attn.fwd_fp8(q8, k8, v8, qs, ks, vs, False, scale, v_transposed=True)
+        v8, vs = attn.quant_per_tensor(v)
+        o, lse = attn.fwd_fp8(q8, k8, v8, qs, ks, vs, False, scale)
     except attn.AttnError as e:
         return {"status": f"not available: {e}"}
     pre_ms, _ = time_launches(lambda: attn.hadamard_quant(q, sg), steps, warmup)
-    vq_ms, _ = time_launches(lambda: attn.quant_per_tensor(v, transposed=True), steps, warmup)
-    att_ms, _ = time_launches(lambda: attn.fwd_fp8(q8, k8, v8, qs, ks, vs, False, scale, v_transposed=True,
-                                                   out=o, lse=lse), steps, warmup)
+    vq_ms, _ = time_launches(lambda: attn.quant_per_tensor(v), steps, warmup)
+    att_ms, _ = time_launches(lambda: attn.fwd_fp8(q8, k8, v8, qs, ks, vs, False, scale, out=o, lse=lse),
+                              steps, warmup)
     fl = flops(B, H, S, S, D, False)
     pre_bytes = B * H * S * D * (2 + 1) + B * H * (S // 64) * 4
     vq_bytes = B * H * S * D * (2 + 2 + 1)

@@ -1,0 +1,308 @@
+// FP8 (OCP E4M3) preparation of attention inputs.
+//
+// hadamard_quant: incoherent processing for Q and K ([NL] "3. Lage precisie
+// (FP8) met reductie van kwantisatiefout": multiply by a random orthogonal
+// matrix before quantizing so outliers spread over all coordinates; [GN]
+// "Niedrige FP8-Praezision und incoherent processing": a random-sign
+// Hadamard transform, O(d log d) per head, bound by memory bandwidth). Per
+// row: u = FWHT(signs * x) in float32, unnormalised, butterfly strides 1, 2,
+// ..., D/2 in that order (every output is the same float32 expression tree as
+// the textbook in-place algorithm, so codes are reproducible bit for bit).
+// Per block of block_rows rows of one (b, h): a = max |u|, inv = 448 / a,
+// code = E4M3(u * inv) rounded to nearest even (the hardware conversion),
+// after clamping to +-448 since the conversion does not saturate; scale =
+// a / 448, times 1/sqrt(D) when the transform is applied.
+//
+// Work split: one workgroup of 256 threads per (b, h, block). A row of D
+// values is spread over D/8 lanes, 8 values (one 16-byte load) per lane;
+// strides 1, 2 and 4 of the transform are in-register, larger strides pair
+// lane L with lane L ^ (stride / 8) through a cross-lane shuffle.
+//
+// quant_per_tensor: one scale for the whole tensor. Launch 1 clears the
+// running maximum, launch 2 reduces max |x| per workgroup and folds it in with
+// an integer atomic max on the float bits (exact for non-negative floats and
+// independent of order, hence deterministic), launch 3 writes the codes,
+// launch 4 turns the maximum into the scale a / 448 (1 if a == 0).
+#include "common.h"
+#include "kernels.h"
+
+namespace attn {
+
+namespace {
+
+constexpr float kE4M3Max = 448.0f;
+
+template <typename T>
+__device__ __forceinline__ void load8(const T* p, float* out) {
+  const uint4 raw = *(const uint4*)p;
+  const T* e = (const T*)&raw;
+#pragma unroll
+  for (int i = 0; i < 8; i++) out[i] = (float)e[i];
+}
+
+// four floats -> four E4M3 codes in one dword (byte i = code of x[i])
+__device__ __forceinline__ uint32_t cvt4(float a, float b, float c, float d) {
+  a = fminf(fmaxf(a, -kE4M3Max), kE4M3Max);
+  b = fminf(fmaxf(b, -kE4M3Max), kE4M3Max);
+  c = fminf(fmaxf(c, -kE4M3Max), kE4M3Max);
+  d = fminf(fmaxf(d, -kE4M3Max), kE4M3Max);
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return (uint32_t)w;
+}
+
+template <typename T, int D>
+__global__ void __launch_bounds__(256)
+hadamard_quant_kernel(const T* __restrict__ X, uint8_t* __restrict__ X8, float* __restrict__ scales,
+                      const signed char* __restrict__ signs, int S, int block_rows, int n_blk,
+                      int apply, float rsqrt_d)
+{
+  constexpr int LPR = D / 8;                 // lanes per row
+  constexpr int RPP = 256 / LPR;             // rows per pass of the workgroup
+  __shared__ float red[4];
+  const int tid = threadIdx.x;
+  const int sub = tid % LPR;                 // position of this lane within its row
+  const int rsub = tid / LPR;
+  const int blk = blockIdx.x % n_blk;
+  const int bh = blockIdx.x / n_blk;
+  const int r0 = blk * block_rows;
+  const int r1 = min(S, r0 + block_rows);
+  const size_t base = (size_t)bh * S * D;
+
+  float sg[8];
+#pragma unroll
+  for (int i = 0; i < 8; i++) sg[i] = apply ? (float)signs[sub * 8 + i] : 1.0f;
+
+  // pass 1: transform every row of the block, track max |u|
+  float amax = 0.0f;
+  for (int r = r0 + rsub; r < r1; r += RPP) {
+    float u[8];
+    load8(X + base + (size_t)r * D + sub * 8, u);
+    if (apply) {
+#pragma unroll
+      for (int i = 0; i < 8; i++) u[i] *= sg[i];
+      // strides 1, 2, 4 inside the lane
+#pragma unroll
+      for (int h = 1; h < 8; h <<= 1)
+#pragma unroll
+        for (int i = 0; i < 8; i++)
+          if ((i & h) == 0) {
+            const float a = u[i], b = u[i + h];
+            u[i] = a + b;
+            u[i + h] = a - b;
+          }
+      // strides 8 .. D/2 across lanes of the row
+#pragma unroll
+      for (int lh = 1; lh < LPR; lh <<= 1) {
+        const bool upper = (sub & lh) != 0;
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+          const float other = __shfl_xor(u[i], lh);
+          u[i] = upper ? other - u[i] : u[i] + other;
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; i++) amax = fmaxf(amax, fabsf(u[i]));
+  }
+  // block maximum
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+  if ((tid & 63) == 0) red[tid >> 6] = amax;
+  __syncthreads();
+  const float a = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const bool nz = a > 0.0f;
+  const float inv = nz ? __fdiv_rn(kE4M3Max, a) : 0.0f;
+
+  // pass 2: recompute (cheap, the block is in cache) and quantize
+  for (int r = r0 + rsub; r < r1; r += RPP) {
+    float u[8];
+    load8(X + base + (size_t)r * D + sub * 8, u);
+    if (apply) {
+#pragma unroll
+      for (int i = 0; i < 8; i++) u[i] *= sg[i];
+#pragma unroll
+      for (int h = 1; h < 8; h <<= 1)
+#pragma unroll
+        for (int i = 0; i < 8; i++)
+          if ((i & h) == 0) {
+            const float x0 = u[i], x1 = u[i + h];
+            u[i] = x0 + x1;
+            u[i + h] = x0 - x1;
+          }
+#pragma unroll
+      for (int lh = 1; lh < LPR; lh <<= 1) {
+        const bool upper = (sub & lh) != 0;
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+          const float other = __shfl_xor(u[i], lh);
+          u[i] = upper ? other - u[i] : u[i] + other;
+        }
+      }
+    }
+    uint2 w = make_uint2(0u, 0u);              // an all-zero block has all-zero codes
+    if (nz) {
+      w.x = cvt4(u[0] * inv, u[1] * inv, u[2] * inv, u[3] * inv);
+      w.y = cvt4(u[4] * inv, u[5] * inv, u[6] * inv, u[7] * inv);
+    }
+    *(uint2*)(X8 + base + (size_t)r * D + sub * 8) = w;
+  }
+  if (tid == 0) {
+    float sc = nz ? __fdiv_rn(a, kE4M3Max) : 1.0f;
+    if (apply && nz) sc = sc * rsqrt_d;
+    scales[(size_t)bh * n_blk + blk] = sc;
+  }
+}
+
+__global__ void clear_u32(uint32_t* p) { *p = 0u; }
+
+template <typename T>
+__global__ void __launch_bounds__(256)
+amax_kernel(const T* __restrict__ X, size_t n8, uint32_t* __restrict__ amax_bits)
+{
+  __shared__ float red[4];
+  float m = 0.0f;
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n8; i += (size_t)gridDim.x * 256) {
+    float v[8];
+    load8(X + i * 8, v);
+#pragma unroll
+    for (int k = 0; k < 8; k++) m = fmaxf(m, fabsf(v[k]));
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const float b = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    atomicMax(amax_bits, __builtin_bit_cast(uint32_t, b));
+  }
+}
+
+template <typename T>
+__global__ void __launch_bounds__(256)
+quant_kernel(const T* __restrict__ X, uint8_t* __restrict__ X8, size_t n8,
+             const uint32_t* __restrict__ amax_bits)
+{
+  const float a = __builtin_bit_cast(float, *amax_bits);
+  const float inv = a > 0.0f ? __fdiv_rn(kE4M3Max, a) : 0.0f;
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n8; i += (size_t)gridDim.x * 256) {
+    float v[8];
+    load8(X + i * 8, v);
+    uint2 w = make_uint2(0u, 0u);
+    if (a > 0.0f) {
+      w.x = cvt4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
+      w.y = cvt4(v[4] * inv, v[5] * inv, v[6] * inv, v[7] * inv);
+    }
+    *(uint2*)(X8 + i * 8) = w;
+  }
+}
+
+// [B, H, S, D] -> codes [B, H, D, S]; one workgroup per (b*h, 64 x 64 tile)
+template <typename T>
+__global__ void __launch_bounds__(256)
+quant_t_kernel(const T* __restrict__ X, uint8_t* __restrict__ X8, int S, int D,
+               const uint32_t* __restrict__ amax_bits)
+{
+  __shared__ uint8_t tile[64][64 + 4];
+  const float a = __builtin_bit_cast(float, *amax_bits);
+  const float inv = a > 0.0f ? __fdiv_rn(kE4M3Max, a) : 0.0f;
+  const int tS = (S + 63) / 64, tD = (D + 63) / 64;
+  const int bh = blockIdx.x / (tS * tD);
+  const int rem = blockIdx.x % (tS * tD);
+  const int s0 = (rem / tD) * 64, d0 = (rem % tD) * 64;
+  const size_t base = (size_t)bh * S * D;
+  // read: 64 rows x 64 columns, 8 columns per thread
+  for (int e = threadIdx.x; e < 64 * 8; e += 256) {
+    const int r = e / 8, c8 = (e % 8) * 8;
+    const int s = s0 + r, d = d0 + c8;
+    if (s < S && d < D) {
+      float v[8];
+      load8(X + base + (size_t)s * D + d, v);
+      const uint32_t w0 = a > 0.0f ? cvt4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv) : 0u;
+      const uint32_t w1 = a > 0.0f ? cvt4(v[4] * inv, v[5] * inv, v[6] * inv, v[7] * inv) : 0u;
+#pragma unroll
+      for (int k = 0; k < 4; k++) {
+        tile[c8 + k][r] = (w0 >> (8 * k)) & 255;
+        tile[c8 + 4 + k][r] = (w1 >> (8 * k)) & 255;
+      }
+    }
+  }
+  __syncthreads();
+  // write: 64 rows (d) x 64 columns (s), 4 bytes per thread
+  for (int e = threadIdx.x; e < 64 * 16; e += 256) {
+    const int dr = e / 16, sc = (e % 16) * 4;
+    const int d = d0 + dr, s = s0 + sc;
+    if (d < D && s < S) {
+      const uint32_t w = tile[dr][sc] | (tile[dr][sc + 1] << 8) | (tile[dr][sc + 2] << 16) |
+                         ((uint32_t)tile[dr][sc + 3] << 24);
+      *(uint32_t*)(X8 + base + (size_t)d * S + s) = w;
+    }
+  }
+}
+
+__global__ void finish_scale_kernel(float* scale_and_bits) {
+  const float a = __builtin_bit_cast(float, *(const uint32_t*)scale_and_bits);
+  *scale_and_bits = a > 0.0f ? __fdiv_rn(a, kE4M3Max) : 1.0f;
+}
+
+template <typename T>
+hipError_t hq_t(const void* x, void* x8, float* scales, const signed char* signs, int B, int H, int S,
+                int D, int block_rows, int apply, hipStream_t st) {
+  const int n_blk = (S + block_rows - 1) / block_rows;
+  const dim3 grid((unsigned)(B * H * n_blk));
+  const float r = (float)(1.0 / __builtin_sqrt((double)D));
+  switch (D) {
+    case 64:
+      hipLaunchKernelGGL((hadamard_quant_kernel<T, 64>), grid, dim3(256), 0, st, (const T*)x, (uint8_t*)x8,
+                         scales, signs, S, block_rows, n_blk, apply, r);
+      break;
+    case 128:
+      hipLaunchKernelGGL((hadamard_quant_kernel<T, 128>), grid, dim3(256), 0, st, (const T*)x, (uint8_t*)x8,
+                         scales, signs, S, block_rows, n_blk, apply, r);
+      break;
+    case 256:
+      hipLaunchKernelGGL((hadamard_quant_kernel<T, 256>), grid, dim3(256), 0, st, (const T*)x, (uint8_t*)x8,
+                         scales, signs, S, block_rows, n_blk, apply, r);
+      break;
+    default:
+      return hipErrorNotSupported;
+  }
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t qpt_t(const void* x, void* x8, float* scale, int B, int H, int S, int D, int transposed,
+                 hipStream_t st) {
+  uint32_t* bits = (uint32_t*)scale;            // the scale slot holds the running max until the end
+  const size_t n8 = (size_t)B * H * S * D / 8;
+  hipLaunchKernelGGL(clear_u32, dim3(1), dim3(1), 0, st, bits);
+  const unsigned grid = (unsigned)(n8 < 2048 * 256 ? (n8 + 255) / 256 : 2048);
+  hipLaunchKernelGGL(amax_kernel<T>, dim3(grid), dim3(256), 0, st, (const T*)x, n8, bits);
+  if (!transposed) {
+    hipLaunchKernelGGL(quant_kernel<T>, dim3(grid), dim3(256), 0, st, (const T*)x, (uint8_t*)x8, n8,
+                       (const uint32_t*)bits);
+  } else {
+    const int tiles = ((S + 63) / 64) * ((D + 63) / 64);
+    hipLaunchKernelGGL(quant_t_kernel<T>, dim3((unsigned)(B * H * tiles)), dim3(256), 0, st, (const T*)x,
+                       (uint8_t*)x8, S, D, (const uint32_t*)bits);
+  }
+  hipLaunchKernelGGL(finish_scale_kernel, dim3(1), dim3(1), 0, st, scale);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_hadamard_quant(const void* x, void* x8, float* scales, const signed char* signs, int B,
+                                 int H, int S, int D, int block_rows, int apply_hadamard, int in_dtype,
+                                 hipStream_t st) {
+  if (in_dtype == 2) return hq_t<__bf16>(x, x8, scales, signs, B, H, S, D, block_rows, apply_hadamard, st);
+  return hq_t<_Float16>(x, x8, scales, signs, B, H, S, D, block_rows, apply_hadamard, st);
+}
+
+hipError_t launch_quant_per_tensor(const void* x, void* x8, float* scale, int B, int H, int S, int D,
+                                   int in_dtype, int write_transposed, hipStream_t st) {
+  if (in_dtype == 2) return qpt_t<__bf16>(x, x8, scale, B, H, S, D, write_transposed, st);
+  return qpt_t<_Float16>(x, x8, scale, B, H, S, D, write_transposed, st);
+}
+
+}  // namespace attn

@@ -145,8 +145,9 @@ int hadamard_quant(const void* x, void* x8, float* scales, const signed char* si
 
 /*
  * quant_per_tensor -- E4M3 quantization with one scale for the whole tensor
- * (two launches: max |x|, then quantize). Used for V on the FP8 path and for
- * the plain per-tensor FP8 baseline without a transform.
+ * (four small launches on `stream`: clear, max |x|, quantize, final scale).
+ * Used for V on the FP8 path and for the plain per-tensor FP8 baseline
+ * without a transform.
  *
  *   x       [B, H, S, D] in_dtype (ATTN_BF16 or ATTN_F16)
  *   x8      uint8 E4M3 codes (written), [B, H, S, D], or [B, H, D, S] when
@@ -167,8 +168,10 @@ int quant_per_tensor(const void* x, void* x8, float* scale, int B, int H, int S,
  *   q8, k8      [B, H, S_q|S_k, D] E4M3 codes
  *   q_scales    [B, H, ceil(S_q / block_rows)] float32 block scales of q8
  *   k_scales    [B, H, ceil(S_k / block_rows)] float32 block scales of k8
- *   v8          E4M3 codes of V, [B, H, S_k, D] (v_transposed = 0) or
- *               [B, H, D, S_k] (v_transposed = 1)
+ *   v8          E4M3 codes of V, [B, H, S_k, D]; v_transposed must be 0 (the
+ *               kernel transposes V in flight with ds_read_b64_tr_b8; the
+ *               [B, H, D, S_k] form that quant_per_tensor can write is
+ *               rejected with ATTN_ERR_UNSUPPORTED)
  *   v_scale     one device float32: the per-tensor scale of v8
  *   o           [B, H, S_q, D] bfloat16 (written); lse [B, H, S_q] float32
  *   block_rows  must be 64 (the key tile of the kernel)
