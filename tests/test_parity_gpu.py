@@ -201,3 +201,18 @@ def test_fullsize_noncausal_d128_8k(gpu_lib):
 def test_fullsize_decode_32k(gpu_lib):
     note("full decode B64 H32 S_q1 S_k32768 D128")
     _fullsize(gpu_lib, 64, 32, 1, 32768, 128, False, heads=4)
+
+
+@pytest.mark.parametrize("dt,D", [(torch.bfloat16, 64), (torch.float16, 128), (torch.bfloat16, 256),
+                                  (torch.bfloat16, 128)])
+@pytest.mark.parametrize("n_split", [2, 5, 13])
+def test_decode_kernel_against_oracle(gpu_lib, dt, D, n_split):
+    B, H, S_k = 2, 3, 5003
+    note(f"decode kernel {dt} D{D} S_k{S_k} splits={n_split}")
+    q, k, v = inputs.qkv(B, H, 1, S_k, D, seed=11, dtype=dt)
+    scale = 1 / math.sqrt(D)
+    for causal in (False, True):
+        o, lse = gpu_lib.fwd(q.cuda(), k.cuda(), v.cuda(), causal=causal, scale=scale, num_splits=n_split)
+        torch.cuda.synchronize()
+        ro, rl = oracle.attention(q.float().numpy(), k.float().numpy(), v.float().numpy(), causal, scale)
+        assert_bf(o, lse, ro, rl, f"decode causal={causal}")
