@@ -121,8 +121,8 @@ def fp8_point(steps=10, warmup=3):
         o, lse = attn.fwd_fp8(q8, k8, v8, qs, ks, vs, False, scale)
     except attn.AttnError as e:
         return {"status": f"not available: {e}"}
-    pre_ms, _ = time_launches(lambda: attn.hadamard_quant(q, sg), steps, warmup)
-    vq_ms, _ = time_launches(lambda: attn.quant_per_tensor(v), steps, warmup)
+    pre_ms, _ = time_launches(lambda: attn.hadamard_quant(q, sg, out=(q8, qs)), steps, warmup)
+    vq_ms, _ = time_launches(lambda: attn.quant_per_tensor(v, out=(v8, vs)), steps, warmup)
     att_ms, _ = time_launches(lambda: attn.fwd_fp8(q8, k8, v8, qs, ks, vs, False, scale, out=o, lse=lse),
                               steps, warmup)
     fl = flops(B, H, S, S, D, False)

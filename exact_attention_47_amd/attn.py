@@ -144,16 +144,24 @@ def check_args(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, H, S_q, S_k, D, causal, s
                                   ctypes.c_float(scale), dtype)
 
 
-def hadamard_quant(x, signs, block_rows=64, apply_hadamard=True):
-    """(codes uint8 [B,H,S,D], scales float32 [B,H,ceil(S/block_rows)])."""
+def hadamard_quant(x, signs, block_rows=64, apply_hadamard=True, out=None):
+    """(codes uint8 [B,H,S,D], scales float32 [B,H,ceil(S/block_rows)]); out=(codes, scales) reuses buffers."""
     _need_gpu(x, signs)
     if x.dim() != 4 or x.dtype not in (torch.bfloat16, torch.float16):
         raise ValueError("x must be a [B, H, S, D] bfloat16/float16 tensor")
     if signs.dtype != torch.int8 or signs.shape != (x.shape[3],):
         raise ValueError("signs must be int8 [D]")
     B, H, S, D = x.shape
-    x8 = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
-    scales = torch.empty((B, H, -(-S // block_rows)), dtype=torch.float32, device=x.device)
+    nb = -(-S // block_rows)
+    if out is None:
+        x8 = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+        scales = torch.empty((B, H, nb), dtype=torch.float32, device=x.device)
+    else:
+        x8, scales = out
+        if (x8.shape != x.shape or x8.dtype != torch.uint8 or scales.shape != (B, H, nb)
+                or scales.dtype != torch.float32 or not (x8.is_contiguous() and scales.is_contiguous())):
+            raise ValueError("out must be contiguous (uint8 [B,H,S,D], float32 [B,H,ceil(S/block_rows)])")
+        _need_gpu(x8, scales)
     st = _stream(x.device)
     _check("hadamard_quant", load().hadamard_quant(_ptr(x), _ptr(x8), _ptr(scales), _ptr(signs), B, H, S,
                                                    D, block_rows, int(bool(apply_hadamard)),
@@ -161,15 +169,22 @@ def hadamard_quant(x, signs, block_rows=64, apply_hadamard=True):
     return x8, scales
 
 
-def quant_per_tensor(x, transposed=False):
-    """(codes uint8 [B,H,S,D] or [B,H,D,S], scale float32 [1])."""
+def quant_per_tensor(x, transposed=False, out=None):
+    """(codes uint8 [B,H,S,D] or [B,H,D,S], scale float32 [1]); out=(codes, scale) reuses buffers."""
     _need_gpu(x)
     if x.dim() != 4 or x.dtype not in (torch.bfloat16, torch.float16):
         raise ValueError("x must be a [B, H, S, D] bfloat16/float16 tensor")
     B, H, S, D = x.shape
     shape = (B, H, D, S) if transposed else (B, H, S, D)
-    x8 = torch.empty(shape, dtype=torch.uint8, device=x.device)
-    scale = torch.empty(1, dtype=torch.float32, device=x.device)
+    if out is None:
+        x8 = torch.empty(shape, dtype=torch.uint8, device=x.device)
+        scale = torch.empty(1, dtype=torch.float32, device=x.device)
+    else:
+        x8, scale = out
+        if (x8.shape != shape or x8.dtype != torch.uint8 or scale.numel() != 1
+                or scale.dtype != torch.float32 or not x8.is_contiguous()):
+            raise ValueError("out must be (contiguous uint8 codes of the output shape, float32 [1])")
+        _need_gpu(x8, scale)
     st = _stream(x.device)
     _check("quant_per_tensor", load().quant_per_tensor(_ptr(x), _ptr(x8), _ptr(scale), B, H, S, D,
                                                        _DTYPE[x.dtype], int(bool(transposed)), st))

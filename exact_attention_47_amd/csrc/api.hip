@@ -185,7 +185,8 @@ int hadamard_quant(const void* x, void* x8, float* scales, const signed char* si
   if (apply_hadamard != 0 && apply_hadamard != 1) return ATTN_ERR_INVALID_ARG;
   if (in_dtype != ATTN_BF16 && in_dtype != ATTN_F16) return ATTN_ERR_INVALID_ARG;
   if (D != 64 && D != 128 && D != 256) return ATTN_ERR_UNSUPPORTED;
-  if (!aligned(x, 16) || !aligned(x8, 16) || !aligned(scales, 4)) return ATTN_ERR_MISALIGNED;
+  if (!aligned(x, 16) || !aligned(x8, 16) || !aligned(scales, 4) || !aligned(signs, 8))
+    return ATTN_ERR_MISALIGNED;
   const hipError_t e = attn::launch_hadamard_quant(x, x8, scales, signs, B, H, S, D, block_rows,
                                                    apply_hadamard, in_dtype, (hipStream_t)stream);
   return e == hipSuccess ? ATTN_OK : (e == hipErrorNotSupported ? ATTN_ERR_UNSUPPORTED : ATTN_ERR_LAUNCH);

@@ -13,10 +13,14 @@
 // after clamping to +-448 since the conversion does not saturate; scale =
 // a / 448, times 1/sqrt(D) when the transform is applied.
 //
-// Work split: one workgroup of 256 threads per (b, h, block). A row of D
-// values is spread over D/8 lanes, 8 values (one 16-byte load) per lane;
-// strides 1, 2 and 4 of the transform are in-register, larger strides pair
-// lane L with lane L ^ (stride / 8) through a cross-lane shuffle.
+// Work split for 64-row blocks (the FP8 attention's block size): one
+// workgroup of 256 threads per (b, h, block), four lanes per row. Lane s of a
+// row holds elements 32k + 8s + i (k < D/32, i < 8), read as D/32 16-byte
+// loads issued together and kept in registers for both passes. Strides 1, 2,
+// 4, 32, 64 and 128 of the transform are then inside the lane and strides 8
+// and 16 are swaps within the 4-lane group (DPP quad permutes, no LDS), still
+// taken in the order 1, 2, ..., D/2. Other block sizes use a general kernel
+// that spreads a row over D/8 lanes and re-reads the block for its second pass.
 //
 // quant_per_tensor: one scale for the whole tensor. Launch 1 clears the
 // running maximum, launch 2 reduces max |x| per workgroup and folds it in with
@@ -154,6 +158,113 @@ hadamard_quant_kernel(const T* __restrict__ X, uint8_t* __restrict__ X8, float* 
   }
 }
 
+// one 64-row block per workgroup, four lanes per row (see the header)
+template <typename T, int D>
+__global__ void __launch_bounds__(256)
+hadamard_quant64_kernel(const T* __restrict__ X, uint8_t* __restrict__ X8, float* __restrict__ scales,
+                        const signed char* __restrict__ signs, int S, int n_blk, int apply, float rsqrt_d)
+{
+  constexpr int NK = D / 32;                 // 8-element chunks per lane
+  __shared__ float red[4];
+  const int tid = threadIdx.x;
+  const int sub = tid & 3;
+  const int blk = blockIdx.x % n_blk;
+  const int bh = blockIdx.x / n_blk;
+  const int r = blk * 64 + (tid >> 2);
+  const bool valid = r < S;
+  const size_t row = ((size_t)bh * S + r) * D;
+
+  float u[NK][8];
+  if (valid) {
+#pragma unroll
+    for (int k = 0; k < NK; k++) load8(X + row + 32 * k + 8 * sub, u[k]);
+  } else {
+#pragma unroll
+    for (int k = 0; k < NK; k++)
+#pragma unroll
+      for (int i = 0; i < 8; i++) u[k][i] = 0.0f;
+  }
+  if (apply) {
+#pragma unroll
+    for (int k = 0; k < NK; k++) {
+      const uint2 sw = *(const uint2*)(signs + 32 * k + 8 * sub);   // eight int8 signs
+#pragma unroll
+      for (int i = 0; i < 8; i++) {
+        const uint32_t byte = ((i < 4 ? sw.x : sw.y) >> (8 * (i & 3))) & 0xffu;
+        const uint32_t neg = (byte >> 7) << 31;                     // -1 -> sign bit set
+        u[k][i] = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, u[k][i]) ^ neg);
+      }
+    }
+    // strides 1, 2, 4: inside each chunk
+#pragma unroll
+    for (int h = 1; h < 8; h <<= 1)
+#pragma unroll
+      for (int k = 0; k < NK; k++)
+#pragma unroll
+        for (int i = 0; i < 8; i++)
+          if ((i & h) == 0) {
+            const float a = u[k][i], b = u[k][i + h];
+            u[k][i] = a + b;
+            u[k][i + h] = a - b;
+          }
+    // strides 8, 16: partner lane sub ^ 1, then sub ^ 2 (quad permutes 1,0,3,2 and 2,3,0,1)
+#pragma unroll
+    for (int lh = 1; lh < 4; lh <<= 1) {
+      const bool upper = (sub & lh) != 0;
+#pragma unroll
+      for (int k = 0; k < NK; k++)
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+          const int v = __builtin_bit_cast(int, u[k][i]);
+          const int o = lh == 1 ? __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false)
+                                : __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false);
+          const float other = __builtin_bit_cast(float, o);
+          u[k][i] = upper ? other - u[k][i] : u[k][i] + other;
+        }
+    }
+    // strides 32, 64, 128: across chunks of the lane
+#pragma unroll
+    for (int h = 1; h < NK; h <<= 1)
+#pragma unroll
+      for (int k = 0; k < NK; k++)
+        if ((k & h) == 0)
+#pragma unroll
+          for (int i = 0; i < 8; i++) {
+            const float a = u[k][i], b = u[k + h][i];
+            u[k][i] = a + b;
+            u[k + h][i] = a - b;
+          }
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int k = 0; k < NK; k++)
+#pragma unroll
+    for (int i = 0; i < 8; i++) amax = fmaxf(amax, fabsf(u[k][i]));
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+  if ((tid & 63) == 0) red[tid >> 6] = amax;
+  __syncthreads();
+  const float a = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const bool nz = a > 0.0f;
+  const float inv = nz ? __fdiv_rn(kE4M3Max, a) : 0.0f;
+  if (valid) {
+#pragma unroll
+    for (int k = 0; k < NK; k++) {
+      uint2 w = make_uint2(0u, 0u);            // an all-zero block has all-zero codes
+      if (nz) {
+        w.x = cvt4(u[k][0] * inv, u[k][1] * inv, u[k][2] * inv, u[k][3] * inv);
+        w.y = cvt4(u[k][4] * inv, u[k][5] * inv, u[k][6] * inv, u[k][7] * inv);
+      }
+      *(uint2*)(X8 + row + 32 * k + 8 * sub) = w;
+    }
+  }
+  if (tid == 0) {
+    float sc = nz ? __fdiv_rn(a, kE4M3Max) : 1.0f;
+    if (apply && nz) sc = sc * rsqrt_d;
+    scales[(size_t)bh * n_blk + blk] = sc;
+  }
+}
+
 __global__ void clear_u32(uint32_t* p) { *p = 0u; }
 
 template <typename T>
@@ -162,7 +273,18 @@ amax_kernel(const T* __restrict__ X, size_t n8, uint32_t* __restrict__ amax_bits
 {
   __shared__ float red[4];
   float m = 0.0f;
-  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n8; i += (size_t)gridDim.x * 256) {
+  const size_t step = (size_t)gridDim.x * 256;
+  size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  for (; i + 3 * step < n8; i += 4 * step) {     // four 16-byte loads in flight per thread
+    float v[4][8];
+#pragma unroll
+    for (int j = 0; j < 4; j++) load8(X + (i + j * step) * 8, v[j]);
+#pragma unroll
+    for (int j = 0; j < 4; j++)
+#pragma unroll
+      for (int k = 0; k < 8; k++) m = fmaxf(m, fabsf(v[j][k]));
+  }
+  for (; i < n8; i += step) {
     float v[8];
     load8(X + i * 8, v);
 #pragma unroll
@@ -185,15 +307,27 @@ quant_kernel(const T* __restrict__ X, uint8_t* __restrict__ X8, size_t n8,
 {
   const float a = __builtin_bit_cast(float, *amax_bits);
   const float inv = a > 0.0f ? __fdiv_rn(kE4M3Max, a) : 0.0f;
-  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n8; i += (size_t)gridDim.x * 256) {
-    float v[8];
-    load8(X + i * 8, v);
+  const size_t step = (size_t)gridDim.x * 256;
+  size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  auto put = [&](size_t c, const float* v) {
     uint2 w = make_uint2(0u, 0u);
     if (a > 0.0f) {
       w.x = cvt4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
       w.y = cvt4(v[4] * inv, v[5] * inv, v[6] * inv, v[7] * inv);
     }
-    *(uint2*)(X8 + i * 8) = w;
+    *(uint2*)(X8 + c * 8) = w;
+  };
+  for (; i + 3 * step < n8; i += 4 * step) {     // four 16-byte loads in flight per thread
+    float v[4][8];
+#pragma unroll
+    for (int j = 0; j < 4; j++) load8(X + (i + j * step) * 8, v[j]);
+#pragma unroll
+    for (int j = 0; j < 4; j++) put(i + j * step, v[j]);
+  }
+  for (; i < n8; i += step) {
+    float v[8];
+    load8(X + i * 8, v);
+    put(i, v);
   }
 }
 
@@ -251,6 +385,24 @@ hipError_t hq_t(const void* x, void* x8, float* scales, const signed char* signs
   const int n_blk = (S + block_rows - 1) / block_rows;
   const dim3 grid((unsigned)(B * H * n_blk));
   const float r = (float)(1.0 / __builtin_sqrt((double)D));
+  if (block_rows == 64) {
+    switch (D) {
+      case 64:
+        hipLaunchKernelGGL((hadamard_quant64_kernel<T, 64>), grid, dim3(256), 0, st, (const T*)x,
+                           (uint8_t*)x8, scales, signs, S, n_blk, apply, r);
+        return hipGetLastError();
+      case 128:
+        hipLaunchKernelGGL((hadamard_quant64_kernel<T, 128>), grid, dim3(256), 0, st, (const T*)x,
+                           (uint8_t*)x8, scales, signs, S, n_blk, apply, r);
+        return hipGetLastError();
+      case 256:
+        hipLaunchKernelGGL((hadamard_quant64_kernel<T, 256>), grid, dim3(256), 0, st, (const T*)x,
+                           (uint8_t*)x8, scales, signs, S, n_blk, apply, r);
+        return hipGetLastError();
+      default:
+        return hipErrorNotSupported;
+    }
+  }
   switch (D) {
     case 64:
       hipLaunchKernelGGL((hadamard_quant_kernel<T, 64>), grid, dim3(256), 0, st, (const T*)x, (uint8_t*)x8,

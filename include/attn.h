@@ -131,6 +131,8 @@ int attn_check_args(const void* q, const void* k, const void* v, const void* o, 
  *            value = E4M3(code) * scale of the code's block
  *   signs    device int8[D], every entry +1 or -1 (values are not checked)
  *   block_rows  1..1024
+ *   x and x8 must be 16-byte aligned, scales 4-byte and signs 8-byte aligned
+ *   (ATTN_ERR_MISALIGNED otherwise)
  *   apply_hadamard  1: transform then quantize; 0: quantize x itself
  *
  * Arithmetic (all float32, so the codes are unique): u = FWHT(signs * x) with

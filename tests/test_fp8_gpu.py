@@ -54,6 +54,36 @@ def test_hadamard_quant_bitexact(gpu_lib, dt, D, apply):
     assert mism == 0, f"{mism} codes differ"
 
 
+@pytest.mark.parametrize("block_rows", [32, 100])
+def test_hadamard_quant_other_block_sizes_bitexact(gpu_lib, block_rows):
+    note(f"hadamard_quant block_rows={block_rows}")
+    B, H, S, D = 1, 2, 333, 128
+    x = inputs.with_outliers((B, H, S, D), 9, inputs.TENSOR_K, dtype=torch.bfloat16)
+    sg = inputs.signs(D, 9)
+    x8, sc = gpu_lib.hadamard_quant(x.cuda(), sg.cuda(), block_rows=block_rows)
+    torch.cuda.synchronize()
+    rc, rs = oracle.hadamard_quantize(x.float().numpy(), sg.numpy(), block_rows)
+    np.testing.assert_array_equal(sc.cpu().numpy().view(np.uint32), rs.astype(np.float32).view(np.uint32))
+    assert int((x8.cpu().numpy() != rc).sum()) == 0
+
+
+def test_hadamard_quant_fullsize_bitexact(gpu_lib):
+    """The FP8 workload's Q tensor (B=2, H=16, S=8192, D=128, outliers), as the bench quantizes it."""
+    note("hadamard_quant full size B2 H16 S8192 D128")
+    B, H, S, D = 2, 16, 8192, 128
+    x = inputs.with_outliers((B, H, S, D), 0, inputs.TENSOR_Q, dtype=torch.bfloat16)
+    sg = inputs.signs(D, 0)
+    xg = x.cuda()
+    x8 = torch.empty((B, H, S, D), dtype=torch.uint8, device="cuda")
+    sc = torch.empty((B, H, S // 64), dtype=torch.float32, device="cuda")
+    for _ in range(2):                       # reused output buffers give the same bytes
+        gpu_lib.hadamard_quant(xg, sg.cuda(), out=(x8, sc))
+    torch.cuda.synchronize()
+    rc, rs = oracle.hadamard_quantize(x.float().numpy(), sg.numpy(), 64)
+    np.testing.assert_array_equal(sc.cpu().numpy().view(np.uint32), rs.astype(np.float32).view(np.uint32))
+    assert int((x8.cpu().numpy() != rc).sum()) == 0
+
+
 @pytest.mark.parametrize("transposed", [False, True])
 def test_quant_per_tensor_bitexact(gpu_lib, transposed):
     note(f"quant_per_tensor transposed={transposed}")
