@@ -166,6 +166,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", choices=["fp8", "decode", "d256", "causal_sweep", "d64_sweep"], default=None,
+                    help="run just this extra workload and print its JSON (for profiling one kernel family)")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="instead of the bench, run K plain device-to-device copies of this many bytes "
                          "(reference for scaling memory-traffic counters)")
@@ -187,6 +189,19 @@ def main():
                           "gbps_read_plus_write": round(2 * args.copy_bytes / ms / 1e6, 1)}), flush=True)
         return
     attn.load()
+    if args.only is not None:
+        st, wu = args.steps, args.warmup
+        runs = {
+            "fp8": lambda: fp8_point(steps=st, warmup=wu),
+            "decode": lambda: decode_point(steps=st, warmup=wu),
+            "d256": lambda: bf16_point(2, 8, 8192, 8192, 256, True, steps=st, warmup=wu),
+            "causal_sweep": lambda: [bf16_point(16384 // n, 16, n, n, 128, True, steps=st, warmup=wu)
+                                     for n in (512, 1024, 2048, 4096, 8192, 16384)],
+            "d64_sweep": lambda: [bf16_point(16384 // n, 32, n, n, 64, False, steps=st, warmup=wu)
+                                  for n in (512, 1024, 2048, 4096, 8192, 16384)],
+        }
+        print(json.dumps({"only": args.only, "result": runs[args.only]()}), flush=True)
+        return
 
     B, H, S, D, causal = 2, 16, 8192, 128, False
     q, k, v = inputs.qkv(B, H, S, S, D, seed=0, dtype=torch.bfloat16, device="cuda")
