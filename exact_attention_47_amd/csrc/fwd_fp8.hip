@@ -70,7 +70,9 @@ __device__ __forceinline__ v16f mma8(v8i a, v8i b, v16f c) {
 }
 
 __device__ __forceinline__ uint32_t pack_fp8(float a, float b, float c, float d) {
-  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  // the first conversion writes the low half and keeps the high half of its
+  // "old" operand, which the second one overwrites: any register will do
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, __builtin_bit_cast(int, d), false);
   w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
   return (uint32_t)w;
 }
@@ -128,27 +130,38 @@ fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ K8, c
     }
   }
 
-  // stage s = K(s), V(s-1) into buffer s & 1, issued by the 256 threads of group 0
+  // stage s = K(s), V(s-1) into buffer s & 1, issued by the 256 threads of
+  // group 0 as buffer loads: 32-bit offsets from per-head resources (rows past
+  // the key range read zeros, whose scores are masked), one add per load.
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)Kh, (short)0, S_k * D8, 0x00020000);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)Vh, (short)0, S_k * D8, 0x00020000);
+  int dma_k[TILE8 / 4096], dma_v[TILE8 / 4096];   // this lane's byte offset within a tile
+#pragma unroll
+  for (int i = 0; i < TILE8 / 4096; i++) {
+    const int r = (i * 4 + wave) * 8 + (lane >> 3);    // 8 rows of 128 bytes per 1 KiB wave load
+    dma_k[i] = r * D8 + (((lane & 7) ^ k8_swz(r)) * 16);
+    dma_v[i] = r * D8 + (((lane & 7) ^ v8_swz(r)) * 16);
+  }
+  // (offsets and destinations go through locals: a target builtin with
+  // template-dependent argument expressions is dropped from the host pass)
   auto issue_stage = [&](int s) {
     char* base = lds + (s & 1) * STAGE8;
-    const int rsub = lane >> 3;                  // 8 rows of 128 bytes per 1 KiB wave load
-    const int u = lane & 7;
-#pragma unroll
-    for (int kv = 0; kv < 2; kv++) {
-      const int t = s - kv;
-      if (t < 0 || t >= n_tiles) continue;
-      const int key0 = t * BN8;
-      const uint8_t* src0 = kv == 0 ? Kh : Vh;
+    if (s < n_tiles) {
+      const int row0 = s * BN8 * D8;
 #pragma unroll
       for (int i = 0; i < TILE8 / 4096; i++) {
-        const int blk = i * 4 + wave;
-        const int r = blk * 8 + rsub;
-        const int cc = u ^ (kv == 0 ? k8_swz(r) : v8_swz(r));
-        const int key = min(key0 + r, S_k - 1);
-        const uint8_t* src = src0 + (size_t)key * D8 + cc * 16;
-        __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)src,
-                                         (void __attribute__((address_space(3)))*)(base + kv * TILE8 + blk * 1024),
-                                         16, 0, 0);
+        char* dst = base + (i * 4 + wave) * 1024;
+        const int off = row0 + dma_k[i];
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (__attribute__((address_space(3))) void*)dst, 16, off, 0, 0, 0);
+      }
+    }
+    if (s >= 1 && s - 1 < n_tiles) {
+      const int row0 = (s - 1) * BN8 * D8;
+#pragma unroll
+      for (int i = 0; i < TILE8 / 4096; i++) {
+        char* dst = base + TILE8 + (i * 4 + wave) * 1024;
+        const int off = row0 + dma_v[i];
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (__attribute__((address_space(3))) void*)dst, 16, off, 0, 0, 0);
       }
     }
   };
@@ -238,12 +251,17 @@ fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ K8, c
             if (!ok) s[kb][4 * i + j] = kNegInf;
           }
     }
+    // running maxima as plain chains, which compile to v_max3 (a pairwise
+    // max of two matrix results costs an extra canonicalizing max each)
     float x0 = kNegInf, x1 = kNegInf;
 #pragma unroll
-    for (int e = 0; e < 16; e++) {
-      x0 = fmaxf(x0, fmaxf(s[0][e], s[1][e]));
-      x1 = fmaxf(x1, fmaxf(s[2][e], s[3][e]));
-    }
+    for (int e = 0; e < 16; e++) x0 = fmaxf(x0, s[0][e]);
+#pragma unroll
+    for (int e = 0; e < 16; e++) x0 = fmaxf(x0, s[1][e]);
+#pragma unroll
+    for (int e = 0; e < 16; e++) x1 = fmaxf(x1, s[2][e]);
+#pragma unroll
+    for (int e = 0; e < 16; e++) x1 = fmaxf(x1, s[3][e]);
     const float x = pair_max(fmaxf(x0 * c0, x1 * c1));
     if (__any(x > m + kTau8)) {
       const float mnew = fmaxf(m, x);
@@ -332,6 +350,7 @@ hipError_t launch_fwd_fp8(const void* q8, const void* k8, const void* v8, const 
                           const float* vs, void* o, float* lse, int B, int H, int S_q, int S_k, int D,
                           int causal, float c, int v_transposed, hipStream_t st) {
   if (D != D8 || v_transposed) return hipErrorNotSupported;
+  if ((long long)(S_k + BN8) * D8 > 0x7fffffffLL) return hipErrorInvalidValue;   // 32-bit buffer offsets
   const int n_qt = (S_q + 255) / 256;
   const dim3 grid((unsigned)(B * H * n_qt));
   if (causal)
