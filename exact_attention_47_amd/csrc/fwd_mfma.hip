@@ -156,28 +156,46 @@ fwd_mfma_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
   // ---- direct global -> LDS loads, issued by the 256 threads of group 0:
   // stage s = K(s) (if s < n_tiles) and V(s-1) (if s >= 1) into buffer s & 1.
   // Each wave instruction fills 1 KiB (RPI rows); lane i lands at byte 16*i
-  // and fetches the logical chunk the swizzle stores there. Rows past the key
-  // range read the last valid key row (their scores are masked).
-  auto issue_stage = [&](int s) {
-    char* base = lds + (s & 1) * C::STAGE;
+  // and fetches the logical chunk the swizzle stores there. The loads are
+  // buffer loads on per-head resources: rows past the end of K or V read
+  // zeros (their scores are masked). The rows a lane loads step by 16 (D=128)
+  // or 32 (D=64) between its instructions, which leaves both swizzles
+  // unchanged, so its part of the offset is one constant and the rest (tile
+  // row and 1 KiB block) is wave-uniform: no vector arithmetic per load.
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)Kh, (short)0, S_k * C::RB, 0x00020000);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)Vh, (short)0, S_k * C::RB, 0x00020000);
+  int lane_k, lane_v;
+  {
     const int rsub = (lane * 16) / C::RB;           // row within the wave instruction
     const int u = ((lane * 16) % C::RB) / 16;       // physical chunk within the row
-#pragma unroll
-    for (int kv = 0; kv < 2; kv++) {
-      const int t = s - kv;                          // K(s) then V(s-1)
-      if (t < 0 || t >= n_tiles) continue;
-      const int key0 = k_lo + t * C::BN;
-      const T* src0 = kv == 0 ? Kh : Vh;
+    const int r = wave * C::RPI + rsub;             // first row; later rows differ by a multiple of 16
+    lane_k = rsub * C::RB + ((u ^ k_swz<D>(r)) * 16);
+    lane_v = rsub * C::RB + ((u ^ v_swz<D>(r)) * 16);
+  }
+  // (offsets and destinations go through locals: a target builtin with
+  // template-dependent argument expressions is dropped from the host pass)
+  auto issue_stage = [&](int s) {
+    char* base = lds + (s & 1) * C::STAGE;
+    if (s < n_tiles) {
+      const int row0 = (k_lo + s * C::BN) * C::RB;
 #pragma unroll
       for (int i = 0; i < 2 * C::NI; i++) {
         const int blk = i * 4 + wave;                // 1 KiB block of the tile
-        const int r = blk * C::RPI + rsub;
-        const int cchunk = u ^ (kv == 0 ? k_swz<D>(r) : v_swz<D>(r));
-        const int key = min(key0 + r, S_k - 1);
-        const T* src = src0 + (size_t)key * D + cchunk * 8;
-        __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)src,
-                                         (void __attribute__((address_space(3)))*)(base + kv * C::TILE + blk * 1024),
-                                         16, 0, 0);
+        char* dst = base + blk * 1024;
+        const int soff = row0 + blk * 1024;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (__attribute__((address_space(3))) void*)dst, 16, lane_k,
+                                                 soff, 0, 0);
+      }
+    }
+    if (s >= 1 && s - 1 < n_tiles) {
+      const int row0 = (k_lo + (s - 1) * C::BN) * C::RB;
+#pragma unroll
+      for (int i = 0; i < 2 * C::NI; i++) {
+        const int blk = i * 4 + wave;
+        char* dst = base + C::TILE + blk * 1024;
+        const int soff = row0 + blk * 1024;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (__attribute__((address_space(3))) void*)dst, 16, lane_v,
+                                                 soff, 0, 0);
       }
     }
   };
@@ -409,6 +427,7 @@ template <> struct Shape<128> { static constexpr int BN = FWD_D128_BN; };
 template <typename T, int D, bool CAUSAL, bool SPLIT>
 static hipError_t launch_one(const FwdArgs& a, hipStream_t st) {
   using C = FwdCfg<D, Shape<D>::BN>;
+  if ((long long)(a.S_k + C::BN) * C::RB > 0x7fffffffLL) return hipErrorInvalidValue;   // 32-bit buffer offsets
   const int n_qt = (a.S_q + C::BM - 1) / C::BM;
   const int n_work = a.B * a.H * n_qt * a.n_split;
   hipLaunchKernelGGL((fwd_mfma_kernel<T, D, Shape<D>::BN, CAUSAL, SPLIT>), dim3(n_work), dim3(C::NT), 0, st,
