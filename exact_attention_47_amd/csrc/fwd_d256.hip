@@ -7,14 +7,19 @@
 // simpler schedule: at D = 256, Q^T (64 VGPRs) and O^T (128 VGPRs) leave too
 // few of the 256 registers of two waves per SIMD for the ping-pong's extra
 // live state, and the matrix work per key tile is four times the softmax
-// work, so a single barrier per tile with register-staged loads suffices.
+// work, so all eight waves run the same phases with one barrier per tile
+// (both waves of a SIMD then issue matrix instructions together).
 //
-// Work split: 8 waves x 32 query rows per workgroup, 32-key tiles, two LDS
-// buffers; the global loads of tile t+1 go to registers before tile t is
-// computed and are written to the other buffer after it. LDS rows are
-// padded (K: 2*D + 16 bytes, V: 2*D + 64 bytes) so that the K reads (16 lanes
-// per cycle over 16 rows) and the transposed V reads (32 lanes per cycle over
-// 4 rows x 64 bytes) fall on distinct banks of the 64-bank LDS.
+// Work split: 8 waves x 32 query rows per workgroup, BN-key tiles, two LDS
+// stages held in two separate arrays (so the compiler can tell a direct load
+// into one from a read of the other; the loop is unrolled by two). Tile t+1
+// is fetched with buffer loads straight into LDS (no registers) while tile t
+// is computed, and waited for before the tile's closing barrier. Rows are
+// stored unpadded with a 16-byte-chunk XOR swizzle (K: chunk ^ (row & 15),
+// V: chunk ^ 4 (row & 3)) so that the K reads (16 lanes per cycle over 16
+// rows) and the transposed V reads (32 lanes per cycle over 4 rows x 64
+// bytes) touch every bank of the 64-bank LDS once. Rows past the end of K/V
+// read zeros (their scores are masked).
 #include "common.h"
 #include "kernels.h"
 
@@ -46,15 +51,13 @@ struct Cfg256 {
   static constexpr int KB = BN / 32;            // 32-key blocks per tile
   static constexpr int DS = D / 16;             // k-steps of the S^T product
   static constexpr int DB = D / 32;             // 32-wide column blocks of O^T
-  static constexpr int CH = D / 8;              // 16-byte chunks per row
-  static constexpr int KS = 2 * D + 16;         // K row stride in LDS (bytes)
-  static constexpr int VS = 2 * D + 64;         // V row stride in LDS (bytes)
-  static constexpr int KT = BN * KS;            // K tile bytes
-  static constexpr int VT = BN * VS;            // V tile bytes
-  static constexpr int STAGE = KT + VT;
-  static constexpr int LDS = 2 * STAGE;
-  static constexpr int NCH = BN * CH / NT;      // 16-byte chunks per thread per tile
-  static_assert(BN * CH % NT == 0, "tile chunks must divide evenly over the threads");
+  static constexpr int RB = 2 * D;              // bytes per K/V row
+  static constexpr int TILE = BN * RB;          // bytes per K or V tile
+  static constexpr int STAGE = 2 * TILE;        // K(t) then V(t)
+  static constexpr int NI = TILE / (NT * 16);   // direct-load instructions per thread per tile
+  static constexpr int RPI = 1024 / RB;         // rows written by one wave instruction
+  static_assert(TILE % (NT * 16) == 0, "tile must split evenly into 1 KiB wave loads");
+  static_assert(RPI * NW % 16 == 0, "a lane's rows must repeat the swizzle between its loads");
 };
 
 constexpr float kTau256 = 8.0f;   // lazy-rescale threshold, log2 domain
@@ -70,7 +73,8 @@ fwd_d256_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
   using C = Cfg256<D, QB, NW, BN>;
   using M = Mma256<T>;
   typedef typename M::frag frag;
-  __shared__ __attribute__((aligned(16))) char lds[C::LDS];
+  __shared__ __attribute__((aligned(1024))) char st0[C::STAGE];
+  __shared__ __attribute__((aligned(1024))) char st1[C::STAGE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -121,39 +125,47 @@ fwd_d256_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
     }
   }
 
-  // ---- global -> register staging of one K/V tile
-  uint4 kst[C::NCH], vst[C::NCH];
-  auto gload = [&](int key0) {
+  // ---- direct loads of one K/V tile: per-head buffer resources, one
+  // lane-constant offset (a lane's rows step by a multiple of 16 between its
+  // loads, which leaves both swizzles unchanged) plus wave-uniform scalars
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)Kh, (short)0, S_k * C::RB, 0x00020000);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)Vh, (short)0, S_k * C::RB, 0x00020000);
+  int lane_k, lane_v;
+  {
+    const int rsub = (lane * 16) / C::RB;
+    const int u = ((lane * 16) % C::RB) / 16;
+    const int r = wave * C::RPI + rsub;
+    lane_k = rsub * C::RB + ((u ^ (r & 15)) * 16);
+    lane_v = rsub * C::RB + ((u ^ (4 * (r & 3))) * 16);
+  }
+  // (offsets and destinations go through locals: a target builtin with
+  // template-dependent argument expressions is dropped from the host pass)
+  auto issue_tile = [&](int key0, char* base) {
 #pragma unroll
-    for (int i = 0; i < C::NCH; i++) {
-      const int id = i * C::NT + tid;
-      const int r = id / C::CH, cc = id % C::CH;
-      const int key = key0 + r;
-      if (key < k_hi) {
-        kst[i] = *(const uint4*)(Kh + (size_t)key * D + cc * 8);
-        vst[i] = *(const uint4*)(Vh + (size_t)key * D + cc * 8);
-      } else {
-        kst[i] = make_uint4(0, 0, 0, 0);
-        vst[i] = make_uint4(0, 0, 0, 0);
-      }
-    }
-  };
-  auto swrite = [&](int buf) {
-    char* kb = lds + buf * C::STAGE;
-    char* vb = kb + C::KT;
-#pragma unroll
-    for (int i = 0; i < C::NCH; i++) {
-      const int id = i * C::NT + tid;
-      const int r = id / C::CH, cc = id % C::CH;
-      *(uint4*)(kb + r * C::KS + cc * 16) = kst[i];
-      *(uint4*)(vb + r * C::VS + cc * 16) = vst[i];
+    for (int i = 0; i < C::NI; i++) {
+      const int blk = i * C::NW + wave;
+      char* kdst = base + blk * 1024;
+      char* vdst = base + C::TILE + blk * 1024;
+      const int soff = key0 * C::RB + blk * 1024;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (__attribute__((address_space(3))) void*)kdst, 16, lane_k,
+                                               soff, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (__attribute__((address_space(3))) void*)vdst, 16, lane_v,
+                                               soff, 0, 0);
     }
   };
 
-  // per-lane LDS bases
-  const int kbase = nn * C::KS + hh * 16;
+  // per-lane LDS read offsets (swizzle folded in; it only reaches the low 4 /
+  // 2 bits of the chunk index, so the offsets repeat every 8 k-steps / 4
+  // column blocks up to a constant)
+  int k_rd[8];
+#pragma unroll
+  for (int ds = 0; ds < 8; ds++) k_rd[ds] = nn * C::RB + (((2 * ds + hh) ^ (nn & 15)) * 16);
   const int g = lane >> 4, jj = lane & 15;
-  const int vbase = (4 * hh + (jj >> 2)) * C::VS + 32 * (g & 1) + 8 * (jj & 3);
+  const int vrow = 4 * hh + (jj >> 2);
+  int v_rd[4];
+#pragma unroll
+  for (int db = 0; db < 4; db++)
+    v_rd[db] = vrow * C::RB + (((4 * db + 2 * (g & 1) + ((jj & 3) >> 1)) ^ (4 * (vrow & 3))) * 16) + 8 * (jj & 1);
 
   v16f o[QB][C::DB];
 #pragma unroll
@@ -166,129 +178,134 @@ fwd_d256_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
 #pragma unroll
   for (int qb = 0; qb < QB; qb++) { m[qb] = kNegInf; l[qb] = 0.0f; }
 
-  if (n_tiles > 0) {
-    gload(k_lo);
-    swrite(0);
-  }
-  __syncthreads();
-
-  for (int t = 0; t < n_tiles; t++) {
+  // one tile: fetch tile t+1 into the other stage, compute tile t, wait for
+  // this wave's loads, barrier
+  auto step = [&](int t, const char* kl, char* nxt) {
     const int key0 = k_lo + t * C::BN;
-    if (t + 1 < n_tiles) gload(key0 + C::BN);
-    const char* kl = lds + (t & 1) * C::STAGE;
-    const char* vl = kl + C::KT;
-
-    // causal: this wave's rows may all precede the tile
-    const bool active = !CAUSAL || key0 <= wr0 + C::RPW - 1 + diag;
-    if (active) {
-      // ---- S^T = K Q^T
-      v16f s[C::KB][QB];
-#pragma unroll
-      for (int kb = 0; kb < C::KB; kb++)
-#pragma unroll
-        for (int qb = 0; qb < QB; qb++)
-#pragma unroll
-          for (int e = 0; e < 16; e++) s[kb][qb][e] = 0.0f;
-#pragma unroll
-      for (int ds = 0; ds < C::DS; ds++) {
-#pragma unroll
-        for (int kb = 0; kb < C::KB; kb++) {
-          const frag a = *(const frag*)(kl + kbase + kb * 32 * C::KS + ds * 32);
-#pragma unroll
-          for (int qb = 0; qb < QB; qb++) s[kb][qb] = M::mma(a, qf[qb][ds], s[kb][qb]);
-        }
-      }
-
-      // ---- mask: keys past the range end, and the causal diagonal
-      const bool need_mask = (key0 + C::BN > k_hi) || (CAUSAL && key0 + C::BN - 1 > wr0 + diag);
-      if (need_mask) {
-#pragma unroll
+    if (t + 1 < n_tiles) issue_tile(key0 + C::BN, nxt);
+    const char* vl = kl + C::TILE;
+      // causal: this wave's rows may all precede the tile
+      const bool active = !CAUSAL || key0 <= wr0 + C::RPW - 1 + diag;
+      if (active) {
+        // ---- S^T = K Q^T
+        v16f s[C::KB][QB];
+  #pragma unroll
         for (int kb = 0; kb < C::KB; kb++)
-#pragma unroll
-          for (int qb = 0; qb < QB; qb++) {
-            const int q = wr0 + qb * 32 + nn;
-#pragma unroll
-            for (int i = 0; i < 4; i++)
-#pragma unroll
-              for (int j = 0; j < 4; j++) {
-                const int key = key0 + kb * 32 + 8 * i + 4 * hh + j;
-                const bool ok = key < k_hi && (!CAUSAL || key <= q + diag);
-                if (!ok) s[kb][qb][4 * i + j] = kNegInf;
-              }
+  #pragma unroll
+          for (int qb = 0; qb < QB; qb++)
+  #pragma unroll
+            for (int e = 0; e < 16; e++) s[kb][qb][e] = 0.0f;
+  #pragma unroll
+        for (int ds = 0; ds < C::DS; ds++) {
+  #pragma unroll
+          for (int kb = 0; kb < C::KB; kb++) {
+            const frag a = *(const frag*)(kl + k_rd[ds % 8] + (ds / 8) * 256 + kb * 32 * C::RB);
+  #pragma unroll
+            for (int qb = 0; qb < QB; qb++) s[kb][qb] = M::mma(a, qf[qb][ds], s[kb][qb]);
           }
-      }
+        }
 
-      // ---- online softmax (base 2, scale folded into c)
-      float mx[QB];
-      bool grow = false;
-#pragma unroll
-      for (int qb = 0; qb < QB; qb++) {
-        float x = kNegInf;
-#pragma unroll
-        for (int kb = 0; kb < C::KB; kb++)
-#pragma unroll
-          for (int e = 0; e < 16; e++) x = fmaxf(x, s[kb][qb][e]);
-        x = pair_max(x) * c;
-        mx[qb] = x;
-        grow |= x > m[qb] + kTau256;
-      }
-      if (__any(grow)) {
-#pragma unroll
+        // ---- mask: keys past the range end, and the causal diagonal
+        const bool need_mask = (key0 + C::BN > k_hi) || (CAUSAL && key0 + C::BN - 1 > wr0 + diag);
+        if (need_mask) {
+  #pragma unroll
+          for (int kb = 0; kb < C::KB; kb++)
+  #pragma unroll
+            for (int qb = 0; qb < QB; qb++) {
+              const int q = wr0 + qb * 32 + nn;
+  #pragma unroll
+              for (int i = 0; i < 4; i++)
+  #pragma unroll
+                for (int j = 0; j < 4; j++) {
+                  const int key = key0 + kb * 32 + 8 * i + 4 * hh + j;
+                  const bool ok = key < k_hi && (!CAUSAL || key <= q + diag);
+                  if (!ok) s[kb][qb][4 * i + j] = kNegInf;
+                }
+            }
+        }
+
+        // ---- online softmax (base 2, scale folded into c)
+        float mx[QB];
+        bool grow = false;
+  #pragma unroll
         for (int qb = 0; qb < QB; qb++) {
-          const float mnew = fmaxf(m[qb], mx[qb]);
-          const float ref = mnew == kNegInf ? 0.0f : mnew;
-          const float alpha = fast_exp2(m[qb] - ref);   // 0 when m was -inf
-          m[qb] = mnew;
-          l[qb] *= alpha;
-#pragma unroll
-          for (int db = 0; db < C::DB; db++)
-#pragma unroll
-            for (int e = 0; e < 16; e++) o[qb][db][e] *= alpha;
+          float x = kNegInf;
+  #pragma unroll
+          for (int kb = 0; kb < C::KB; kb++)
+  #pragma unroll
+            for (int e = 0; e < 16; e++) x = fmaxf(x, s[kb][qb][e]);
+          x = pair_max(x) * c;
+          mx[qb] = x;
+          grow |= x > m[qb] + kTau256;
         }
-      }
-#pragma unroll
-      for (int qb = 0; qb < QB; qb++) {
-        const float ref = m[qb] == kNegInf ? 0.0f : m[qb];
-        float ls = 0.0f;
-#pragma unroll
-        for (int kb = 0; kb < C::KB; kb++)
-#pragma unroll
-          for (int e = 0; e < 16; e++) {
-            const float p = fast_exp2(__builtin_fmaf(s[kb][qb][e], c, -ref));
-            s[kb][qb][e] = p;
-            ls += p;
-          }
-        l[qb] += ls;
-      }
-
-      // ---- O^T += V^T P^T
-#pragma unroll
-      for (int kb = 0; kb < C::KB; kb++)
-#pragma unroll
-        for (int ks = 0; ks < 2; ks++) {
-          frag pf[QB];
-#pragma unroll
+        if (__any(grow)) {
+  #pragma unroll
           for (int qb = 0; qb < QB; qb++) {
-            v8f x;
-#pragma unroll
-            for (int e = 0; e < 8; e++) x[e] = s[kb][qb][8 * ks + e];
-            pf[qb] = M::cvt(x);
-          }
-#pragma unroll
-          for (int db = 0; db < C::DB; db++) {
-            const int off = (kb * 32 + 16 * ks) * C::VS + db * 64;
-            v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vl + vbase + off));
-            v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vl + vbase + off + 8 * C::VS));
-            v8i16 a16 = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-            const frag a = __builtin_bit_cast(frag, a16);
-#pragma unroll
-            for (int qb = 0; qb < QB; qb++) o[qb][db] = M::mma(a, pf[qb], o[qb][db]);
+            const float mnew = fmaxf(m[qb], mx[qb]);
+            const float ref = mnew == kNegInf ? 0.0f : mnew;
+            const float alpha = fast_exp2(m[qb] - ref);   // 0 when m was -inf
+            m[qb] = mnew;
+            l[qb] *= alpha;
+  #pragma unroll
+            for (int db = 0; db < C::DB; db++)
+  #pragma unroll
+              for (int e = 0; e < 16; e++) o[qb][db][e] *= alpha;
           }
         }
-    }
+  #pragma unroll
+        for (int qb = 0; qb < QB; qb++) {
+          const float ref = m[qb] == kNegInf ? 0.0f : m[qb];
+          float ls = 0.0f;
+  #pragma unroll
+          for (int kb = 0; kb < C::KB; kb++)
+  #pragma unroll
+            for (int e = 0; e < 16; e++) {
+              const float p = fast_exp2(__builtin_fmaf(s[kb][qb][e], c, -ref));
+              s[kb][qb][e] = p;
+              ls += p;
+            }
+          l[qb] += ls;
+        }
 
-    if (t + 1 < n_tiles) swrite((t + 1) & 1);
+        // ---- O^T += V^T P^T
+  #pragma unroll
+        for (int kb = 0; kb < C::KB; kb++)
+  #pragma unroll
+          for (int ks = 0; ks < 2; ks++) {
+            frag pf[QB];
+  #pragma unroll
+            for (int qb = 0; qb < QB; qb++) {
+              v8f x;
+  #pragma unroll
+              for (int e = 0; e < 8; e++) x[e] = s[kb][qb][8 * ks + e];
+              pf[qb] = M::cvt(x);
+            }
+  #pragma unroll
+            for (int db = 0; db < C::DB; db++) {
+              const char* va = vl + v_rd[db % 4] + (db / 4) * 256 + (kb * 32 + 16 * ks) * C::RB;
+              v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)va);
+              v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(va + 8 * C::RB));
+              v8i16 a16 = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+              const frag a = __builtin_bit_cast(frag, a16);
+  #pragma unroll
+              for (int qb = 0; qb < QB; qb++) o[qb][db] = M::mma(a, pf[qb], o[qb][db]);
+            }
+          }
+      }
+
+    __builtin_amdgcn_s_waitcnt(0x0070 | 0x0F00);   // vmcnt(0): this wave's share of tile t+1
     __syncthreads();
+  };
+  if (n_tiles > 0) {
+    issue_tile(k_lo, st0);
+    __builtin_amdgcn_s_waitcnt(0x0070 | 0x0F00);
+    __syncthreads();
+    int t = 0;
+    for (; t + 1 < n_tiles; t += 2) {
+      step(t, st0, st1);
+      step(t + 1, st1, st0);
+    }
+    if (t < n_tiles) step(t, st0, st1);
   }
 
   // ---- epilogue: normalise, logsumexp, store
@@ -335,12 +352,17 @@ fwd_d256_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
 
 // ---------------------------------------------------------------- launcher
 
+#ifndef D256_BN
+#define D256_BN 32
+#endif
+
 template <typename T, bool CAUSAL, bool SPLIT>
 static hipError_t launch_256(const FwdArgs& a, hipStream_t st) {
-  using C = Cfg256<256, 1, 8, 32>;
+  using C = Cfg256<256, 1, 8, D256_BN>;
+  if ((long long)(a.S_k + C::BN) * C::RB > 0x7fffffffLL) return hipErrorInvalidValue;   // 32-bit buffer offsets
   const int n_qt = (a.S_q + C::BM - 1) / C::BM;
   const int n_work = a.B * a.H * n_qt * a.n_split;
-  hipLaunchKernelGGL((fwd_d256_kernel<T, 256, 1, 8, 32, CAUSAL, SPLIT>), dim3(n_work), dim3(C::NT), 0, st,
+  hipLaunchKernelGGL((fwd_d256_kernel<T, 256, 1, 8, D256_BN, CAUSAL, SPLIT>), dim3(n_work), dim3(C::NT), 0, st,
                      (const T*)a.q, (const T*)a.k, (const T*)a.v, (T*)a.o, a.lse, a.opart, a.lpart,
                      a.B * a.H, a.S_q, a.S_k, n_qt, a.n_split, a.keys_per_split, a.c);
   return hipGetLastError();
@@ -353,7 +375,7 @@ static hipError_t launch_256_t(const FwdArgs& a, hipStream_t st) {
   return split ? launch_256<T, false, true>(a, st) : launch_256<T, false, false>(a, st);
 }
 
-int d256_keys_per_tile() { return 32; }
+int d256_keys_per_tile() { return D256_BN; }
 
 hipError_t launch_fwd_d256(const FwdArgs& a, hipStream_t st) {
   if (a.dtype == 2) return launch_256_t<__bf16>(a, st);
