@@ -56,6 +56,14 @@ Plan plan_splits(int dtype, int B, int H, int S_q, int S_k, int D, int req) {
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// Causal D = 128 attention over at most 2048 keys runs on the short-range
+// kernel (measured faster there: two workgroups per CU hide the start-up of
+// each other's few tiles); everything else on the main kernel. Requested
+// splits always go to the main kernel, whose key tile the split plan uses.
+bool use_short_kernel(int D, int causal, int S_k, int n_split) {
+  return D == 128 && causal && S_k <= 2048 && n_split == 1;
+}
+
 size_t ws_bytes(const Plan& p, int B, int H, int S_q, int D) {
   if (p.n_split <= 1) return 0;
   const size_t rows = (size_t)p.n_split * B * H * S_q;
@@ -111,6 +119,7 @@ int run_fwd(const void* q, const void* k, const void* v, void* o, float* lse, in
   hipError_t e;
   if (dtype == ATTN_F32) e = attn::launch_fwd_f32(a, st);
   else if (p.n_split > 1 && S_q <= attn::decode_max_rows()) e = attn::launch_fwd_decode(a, st);
+  else if (use_short_kernel(D, causal, S_k, p.n_split)) e = attn::launch_fwd_short(a, st);
   else e = attn::launch_fwd_mfma(a, st);
   if (e == hipSuccess && p.n_split > 1) e = attn::launch_combine(a, st);
   if (need > 0 && own_ws) {

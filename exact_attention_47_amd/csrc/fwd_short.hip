@@ -1,0 +1,517 @@
+// Fused exact attention forward pass for short causal sequences (bf16 / fp16,
+// D = 64 / 128): two co-resident workgroups per CU, each wave software-pipelined.
+//
+// Same method as the main kernel (O = softmax(scale Q K^T [+ causal]) V and
+// the row logsumexp by tiles with online softmax rescaling, [NL]
+// "FlashAttention en FlashAttention-2"; [GN] "Rueckblick auf den
+// FlashAttention-Ansatz") and the same transposed operand layout (S^T = K Q^T,
+// O^T = V^T P^T, one lane per query row, base-2 softmax, lazy rescaling).
+// What changes is the schedule, for key ranges of a few tiles, where the main
+// kernel's one workgroup per CU leaves its start-up latency and memory waits
+// exposed:
+//
+// * 4 waves x 32 query rows per workgroup and 32-key tiles, so three LDS
+//   stages take 48 KiB and two workgroups fit on a CU (204 VGPRs per lane,
+//   one wave of each per SIMD): while one waits on memory the other computes.
+//
+// * Overlap inside each wave ([GN] "Overlap innerhalb einer Warpgroup"):
+//   step t computes S(t+1) = K(t+1) Q^T with the exponentials of tile t spread
+//   between its matrix instructions, then O += V(t)^T P(t)^T with the row
+//   maximum of tile t+1 in between. Each step is straight-line code with a
+//   scheduling barrier per matrix instruction: tiles that need a mask (the
+//   key-range tail, the causal diagonal) are always a suffix of a wave's
+//   tiles and run in a second unrolled loop; scores past the range are -inf
+//   instead of skipped; a row-maximum increase is applied to O at the next
+//   step, after that tile's P V (still exact).
+//
+// * Stage j = {K(j), V(j-1)} lives in one of three separate __shared__ arrays
+//   (so the compiler can tell the direct load into one from the reads of
+//   another; the loop is unrolled by three). Stage t+3 is fetched with buffer
+//   loads into the array that step t-1 finished with, and waited for at the
+//   end of step t+1.
+#include "common.h"
+#include "kernels.h"
+
+
+namespace attn {
+
+namespace {
+
+template <typename T> struct Mma;
+template <> struct Mma<__bf16> {
+  typedef v8bf16 frag;
+  static __device__ __forceinline__ v16f mma(frag a, frag b, v16f c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ frag cvt(v8f x) { return __builtin_convertvector(x, v8bf16); }
+};
+template <> struct Mma<_Float16> {
+  typedef v8f16 frag;
+  static __device__ __forceinline__ v16f mma(frag a, frag b, v16f c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ frag cvt(v8f x) { return __builtin_convertvector(x, v8f16); }
+};
+
+template <int D>
+struct ShortCfg {
+  static constexpr int NW = 4;                  // waves per workgroup (one per SIMD)
+  static constexpr int NT = NW * 64;
+  static constexpr int BM = NW * 32;            // query rows per workgroup
+  static constexpr int BN = 32;                 // keys per tile
+  static constexpr int KB = BN / 32;            // 32-key blocks per tile
+  static constexpr int DS = D / 16;             // k-steps of the S^T product
+  static constexpr int DB = D / 32;             // 32-wide column blocks of O^T
+  static constexpr int RB = 2 * D;              // bytes per K/V row
+  static constexpr int TILE = BN * RB;          // bytes per K or V tile
+  static constexpr int STAGE = 2 * TILE;        // K(j) then V(j-1)
+  static constexpr int NI = TILE / (NT * 16);   // direct-load instructions per thread per tile
+  static constexpr int RPI = 1024 / RB;         // rows written by one wave instruction
+  static_assert(TILE % (NT * 16) == 0, "tile must split evenly into 1 KiB wave loads");
+};
+
+// Row-dependent 16-byte-chunk XOR swizzles of the K and V tiles.
+template <int D> __device__ __forceinline__ int k_swz(int r) { return D == 64 ? (r >> 1) & 7 : r & 15; }
+template <int D> __device__ __forceinline__ int v_swz(int r) { return D == 64 ? 4 * ((r >> 1) & 1) : 4 * (r & 3); }
+
+constexpr float kTau = 8.0f;   // lazy-rescale threshold, log2 domain
+
+// scheduling groups (instruction classes of __builtin_amdgcn_sched_group_barrier)
+#define SGB(mask, n) __builtin_amdgcn_sched_group_barrier(mask, n, 0)
+constexpr int kMFMA = 0x008, kVALU = 0x002 | 0x400, kDSR = 0x100;
+#ifndef LA_S
+#define LA_S 3
+#endif
+#ifndef LA_P
+#define LA_P 3
+#endif
+#ifndef VPS
+#define VPS 7
+#endif
+#ifndef VPP
+#define VPP 2
+#endif
+
+template <int N> struct IC { static constexpr int value = N; };
+
+template <typename T, int D, bool CAUSAL, bool SPLIT>
+__global__ void __launch_bounds__(256)
+__attribute__((amdgpu_waves_per_eu(2, 2)))
+fwd_short_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
+                T* __restrict__ O, float* __restrict__ LSE,
+                float* __restrict__ Opart, float* __restrict__ Lpart,
+                int BH, int S_q, int S_k, int n_qt, int n_split, int keys_per_split, float c)
+{
+  using C = ShortCfg<D>;
+  using M = Mma<T>;
+  typedef typename M::frag frag;
+  // three stage buffers as separate objects, so that the compiler can tell a
+  // direct load into one from a read of another
+  __shared__ __attribute__((aligned(1024))) char st0[C::STAGE];
+  __shared__ __attribute__((aligned(1024))) char st1[C::STAGE];
+  __shared__ __attribute__((aligned(1024))) char st2[C::STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hh = lane >> 5;        // lane half
+  const int nn = lane & 31;        // query column owned by this lane
+
+  // ---- which (b*h, q tile, split) this workgroup computes
+  const int n_work = BH * n_qt * n_split;
+  int work = xcd_swizzle(blockIdx.x, n_work);
+  const int split = work % n_split;
+  work /= n_split;
+  int qt = work % n_qt;
+  const int bh = work / n_qt;
+  if (CAUSAL) qt = n_qt - 1 - qt;  // heaviest query tiles first
+
+  const int q0 = qt * C::BM;
+  const int wr0 = q0 + wave * 32;              // first row of this wave
+  const int diag = S_k - S_q;                  // causal: key j allowed iff j <= i + diag
+  int k_lo = 0, k_hi = S_k;
+  if (SPLIT) {
+    k_lo = split * keys_per_split;
+    k_hi = min(S_k, k_lo + keys_per_split);
+  }
+  int k_end = k_hi;
+  if (CAUSAL) k_end = min(k_end, q0 + C::BM - 1 + diag + 1);
+  const int n_tiles = k_end > k_lo ? (k_end - k_lo + C::BN - 1) / C::BN : 0;
+
+  const size_t qoff = (size_t)bh * S_q * D;
+  const size_t koff = (size_t)bh * S_k * D;
+  const T* Qh = Q + qoff;
+  const T* Kh = K + koff;
+  const T* Vh = V + koff;
+
+  // ---- Q^T fragments (B operand of S^T), kept in registers
+  frag qf[C::DS];
+  {
+    const int q = wr0 + nn;
+#pragma unroll
+    for (int ds = 0; ds < C::DS; ds++) {
+      if (q < S_q) {
+        qf[ds] = *(const frag*)(Qh + (size_t)q * D + ds * 16 + 8 * hh);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; e++) qf[ds][e] = (T)0.0f;
+      }
+    }
+  }
+
+  // ---- direct global -> LDS loads: stage j = K(j) and V(j-1). Every wave
+  // issues its share (NI instructions per tile, 1 KiB each, lane i landing at
+  // byte 16*i and fetching the logical chunk the swizzle stores there), as
+  // buffer loads on per-head resources: rows outside K/V read zeros (their
+  // scores are masked, or the tile is never read), and every stage issues the
+  // same number of instructions, which keeps the wait counts exact.
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)Kh, (short)0, S_k * C::RB, 0x00020000);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)Vh, (short)0, S_k * C::RB, 0x00020000);
+  const int dma_rsub = (lane * 16) / C::RB;
+  const int dma_u = ((lane * 16) % C::RB) / 16;
+  // (offsets and destinations go through locals: a target builtin with
+  // template-dependent argument expressions is dropped from the host pass)
+  auto issue_stage = [&](int j, char* base) {
+    const int krow0 = k_lo + j * C::BN;               // may be negative or past the end: reads 0
+#pragma unroll
+    for (int i = 0; i < C::NI; i++) {
+      const int blk = i * C::NW + wave;
+      const int r = blk * C::RPI + dma_rsub;
+      const int koff = (krow0 + r) * C::RB + ((dma_u ^ k_swz<D>(r)) * 16);
+      const int voff = (krow0 - C::BN + r) * C::RB + ((dma_u ^ v_swz<D>(r)) * 16);
+      char* kdst = base + blk * 1024;
+      char* vdst = base + C::TILE + blk * 1024;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (__attribute__((address_space(3))) void*)kdst, 16, koff, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (__attribute__((address_space(3))) void*)vdst, 16, voff, 0, 0, 0);
+    }
+  };
+
+  // ---- per-lane LDS read offsets (swizzle folded in)
+  constexpr int NKR = C::DS < 8 ? C::DS : 8;
+  constexpr int NVR = C::DB < 4 ? C::DB : 4;
+  const int xk = k_swz<D>(nn);
+  int k_rd[NKR];
+#pragma unroll
+  for (int ds = 0; ds < NKR; ds++) k_rd[ds] = nn * C::RB + (((2 * ds + hh) ^ xk) * 16);
+  const int g = lane >> 4, jj = lane & 15;
+  const int vrow = 4 * hh + (jj >> 2);
+  const int xv = v_swz<D>(vrow);
+  int v_rd[NVR];
+#pragma unroll
+  for (int db = 0; db < NVR; db++)
+    v_rd[db] = vrow * C::RB + (((4 * db + 2 * (g & 1) + ((jj & 3) >> 1)) ^ xv) * 16) + 8 * (jj & 1);
+
+  v16f o[C::DB];
+#pragma unroll
+  for (int db = 0; db < C::DB; db++)
+#pragma unroll
+    for (int e = 0; e < 16; e++) o[db][e] = 0.0f;
+  v16f sacc[3][C::KB];             // scores of tiles j, j+1 (index j % 3)
+#pragma unroll
+  for (int kb = 0; kb < C::KB; kb++)
+#pragma unroll
+    for (int e = 0; e < 16; e++) sacc[2][kb][e] = kNegInf;   // "tile -1"
+  frag pf[C::KB][2];
+  float m = kNegInf, l = 0.0f, rf = 0.0f, alpha = 1.0f;
+  bool resc = false;
+
+  auto tile_active = [&](int t) { return !CAUSAL || k_lo + t * C::BN <= wr0 + 31 + diag; };
+
+  auto mask = [&](v16f* sn, int t) {
+    const int key0 = k_lo + t * C::BN;
+    {
+      const int q = wr0 + nn;
+#pragma unroll
+      for (int kb = 0; kb < C::KB; kb++)
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+#pragma unroll
+          for (int jx = 0; jx < 4; jx++) {
+            const int key = key0 + kb * 32 + 8 * i + 4 * hh + jx;
+            const bool ok = key < k_hi && (!CAUSAL || key <= q + diag);
+            if (!ok) sn[kb][4 * i + jx] = kNegInf;
+          }
+    }
+  };
+  // row maximum of a new tile: decide whether the reference moves (applied to
+  // O and l once the previous tile's P V is in)
+  float xmax = kNegInf;
+  auto maxdec_b = [&] {
+    const float x = xmax;
+    resc = __any(x > m + kTau);
+    if (resc) {
+      const float mnew = fmaxf(m, x);
+      const float r = mnew == kNegInf ? 0.0f : mnew;
+      alpha = fast_exp2(m - r);            // 0 when m was -inf
+      m = mnew;
+      rf = r;
+    }
+  };
+  // S(t+1)^T = K Q^T with the exponentials of tile t spread over its steps:
+  // each step loads the K fragment LA steps ahead, issues one MFMA and a
+  // fixed share of the vector work; a scheduling barrier keeps that order
+  // (and the register footprint) fixed.
+  constexpr int LA = 3;
+  auto sblock = [&](const char* st, v16f* sd, const v16f* sc) {
+    constexpr bool DS_ = true, DE = true;
+    constexpr int NS = C::DS * C::KB;
+    constexpr int EPS = 16 * C::KB / NS;         // exponentials per step
+    auto load = [&](int j) {
+      const int kb = j / C::DS, ds = j % C::DS;
+      return *(const frag*)(st + k_rd[ds % NKR] + (ds / NKR) * 256 + kb * 32 * C::RB);
+    };
+    frag ring[LA + 1];
+    if (DS_) {
+#pragma unroll
+      for (int j = 0; j < LA; j++) ring[j] = load(j);
+    }
+    float ls = 0.0f;
+    v8f pv;
+#pragma unroll
+    for (int j = 0; j < NS; j++) {
+      if (DS_) {
+        if (j + LA < NS) ring[(j + LA) % (LA + 1)] = load(j + LA);
+        const int kb = j / C::DS, ds = j % C::DS;
+        if (ds == 0) {
+          const v16f zero = {};
+          sd[kb] = M::mma(ring[j % (LA + 1)], qf[ds], zero);
+        } else {
+          sd[kb] = M::mma(ring[j % (LA + 1)], qf[ds], sd[kb]);
+        }
+      }
+      if (DE) {
+#pragma unroll
+        for (int u = 0; u < EPS; u++) {
+          const int idx = j * EPS + u, gi = idx / 8, e = idx % 8;
+          const float p = fast_exp2(__builtin_fmaf(sc[gi / 2][8 * (gi % 2) + e], c, -rf));
+          pv[e] = p;
+          ls += p;
+          if (e == 7) pf[gi / 2][gi % 2] = M::cvt(pv);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    return ls;
+  };
+  // O^T += V(t)^T P(t)^T with the row maximum of tile t+1 spread over its steps
+  auto pblock = [&](auto do_m, const char* st, const v16f* sn) {
+    constexpr bool DP = true, DM = decltype(do_m)::value;
+    constexpr int NP = C::KB * 2 * C::DB;
+    constexpr int MPS = 16 * C::KB / NP;         // score elements per step
+    const char* vl = st + C::TILE;
+    auto load = [&](int j) {
+      const int kb = j / (2 * C::DB), ks = (j / C::DB) % 2, db = j % C::DB;
+      const int off = (kb * 32 + 16 * ks) * C::RB;
+      const char* va = vl + v_rd[db % NVR] + (db / NVR) * 256 + off;
+      v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)va);
+      v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(va + 8 * C::RB));
+      return __builtin_bit_cast(frag, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    frag ring[LA + 1];
+    if (DP) {
+#pragma unroll
+      for (int j = 0; j < LA; j++) ring[j] = load(j);
+    }
+    float x = kNegInf;
+#pragma unroll
+    for (int j = 0; j < NP; j++) {
+      if (DP) {
+        if (j + LA < NP) ring[(j + LA) % (LA + 1)] = load(j + LA);
+        const int kb = j / (2 * C::DB), ks = (j / C::DB) % 2, db = j % C::DB;
+        o[db] = M::mma(ring[j % (LA + 1)], pf[kb][ks], o[db]);
+      }
+      if (DM) {
+#pragma unroll
+        for (int u = 0; u < MPS; u++) {
+          const int idx = j * MPS + u;
+          x = fmaxf(x, sn[idx / 16][idx % 16]);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (DM) xmax = pair_max(x) * c;
+  };
+  auto barrier = [] {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+  };
+
+  // One step t (-1 <= t < n_tiles) of every wave: stage t+1 (K(t+1), V(t))
+  // is read from buffer (t+1) % 3 while stage t+3 is fetched into buffer t % 3.
+  //   S(t+1)^T = K(t+1) Q^T   with the exponentials of tile t in between;
+  //   O^T += V(t)^T P(t)^T    with the mask and row maximum of tile t+1.
+  // The two waves on a SIMD (one from each resident workgroup) both run this
+  // mix, so matrix instructions of one issue while the other's vector
+  // instructions run.
+  auto step = [&](auto bi, auto masked, int t) {
+    constexpr int B = decltype(bi)::value;
+    constexpr bool MASKED = decltype(masked)::value;
+    char* dbuf = B == 0 ? st0 : B == 1 ? st1 : st2;
+    const char* rbuf = B == 0 ? st1 : B == 1 ? st2 : st0;
+    v16f* scur = sacc[B];
+    v16f* snx = sacc[(B + 1) % 3];
+    barrier();
+    issue_stage(t + 3, dbuf);
+    if (resc) {
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < C::DB; db++)
+#pragma unroll
+        for (int e = 0; e < 16; e++) o[db][e] *= alpha;
+    }
+    l += sblock(rbuf, snx, scur);
+    if (MASKED) {
+      mask(snx, t + 1);
+      pblock(IC<0>(), rbuf, snx);
+      float x = kNegInf;
+#pragma unroll
+      for (int kb = 0; kb < C::KB; kb++)
+#pragma unroll
+        for (int e = 0; e < 16; e++) x = fmaxf(x, snx[kb][e]);
+      xmax = pair_max(x) * c;
+    } else {
+      pblock(IC<1>(), rbuf, snx);
+    }
+    maxdec_b();
+    __builtin_amdgcn_s_waitcnt(0x0070 | 0x0F00 | (2 * C::NI));   // stage t+2 complete
+  };
+
+  // Steps run from t = -1 to the wave's last tile with any allowed key
+  // (causal: a prefix of the tiles); scores of tiles past the key range are
+  // masked to -inf, and before the first tile the "current" scores are -inf,
+  // so their probabilities are exactly 0 and every step is the same code.
+  // After its last tile a wave only keeps the barriers and its share of the
+  // loads going until the workgroup's last tile.
+  if (n_tiles > 0) {
+    int t_last = n_tiles - 1;
+    if (CAUSAL) {
+      const int lim = wr0 + 31 + diag - k_lo;
+      t_last = lim < 0 ? -1 : min(t_last, lim / C::BN);
+    }
+    issue_stage(0, st0);
+    issue_stage(1, st1);
+    __builtin_amdgcn_s_waitcnt(0x0070 | 0x0F00);
+    __syncthreads();
+    // tiles whose scores need no mask for any row of this wave come first;
+    // the masked ones (key-range tail, causal diagonal) are a suffix
+    int u_mask = (k_hi - k_lo) / C::BN;
+    if (CAUSAL) {
+      const int lim2 = wr0 + diag - k_lo + 1;
+      u_mask = min(u_mask, lim2 < 0 ? 0 : lim2 / C::BN);
+    }
+    const IC<0> P;
+    const IC<1> Mk;
+    int t = -1;
+    const int t_plain = min(t_last, u_mask - 2);      // last step whose new tile is unmasked
+    for (; t + 2 <= t_plain; t += 3) {
+      step(IC<2>(), P, t);
+      step(IC<0>(), P, t + 1);
+      step(IC<1>(), P, t + 2);
+    }
+    for (; t + 2 <= t_last; t += 3) {
+      step(IC<2>(), Mk, t);
+      step(IC<0>(), Mk, t + 1);
+      step(IC<1>(), Mk, t + 2);
+    }
+    if (t <= t_last) { step(IC<2>(), Mk, t); t++; }
+    if (t <= t_last) { step(IC<0>(), Mk, t); t++; }
+    for (; t < n_tiles; t++) {
+      const int bsel = (t + 3) % 3;
+      barrier();
+      issue_stage(t + 3, bsel == 0 ? st0 : bsel == 1 ? st1 : st2);
+      __builtin_amdgcn_s_waitcnt(0x0070 | 0x0F00 | (2 * C::NI));
+    }
+    __builtin_amdgcn_s_waitcnt(0x0070 | 0x0F00);
+    if (resc) {                    // a reference change not yet applied (cannot happen: the
+      l *= alpha;                  // last scores a wave looks at are fully masked)
+#pragma unroll
+      for (int db = 0; db < C::DB; db++)
+#pragma unroll
+        for (int e = 0; e < 16; e++) o[db][e] *= alpha;
+    }
+  }
+
+  // ---- epilogue: normalise, logsumexp, store
+  const int q = wr0 + nn;
+  const float lt = pair_sum(l);
+  const bool has = m != kNegInf && lt > 0.0f;
+  const float inv = has ? 1.0f / lt : 0.0f;
+  const float lse = has ? (m + __builtin_log2f(lt)) * kLn2 : kNegInf;
+  if (q < S_q) {
+    if (!SPLIT) {
+      T* orow = O + qoff + (size_t)q * D;
+#pragma unroll
+      for (int db = 0; db < C::DB; db++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          typedef T v4t __attribute__((ext_vector_type(4)));
+          v4t w;
+#pragma unroll
+          for (int j = 0; j < 4; j++) w[j] = (T)(o[db][4 * i + j] * inv);
+          *(v4t*)(orow + db * 32 + 8 * i + 4 * hh) = w;
+        }
+      if (hh == 0) LSE[(size_t)bh * S_q + q] = lse;
+    } else {
+      const size_t prow = ((size_t)split * BH + bh) * S_q + q;
+      float* orow = Opart + prow * D;
+#pragma unroll
+      for (int db = 0; db < C::DB; db++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          float4 w;
+          w.x = o[db][4 * i + 0] * inv;
+          w.y = o[db][4 * i + 1] * inv;
+          w.z = o[db][4 * i + 2] * inv;
+          w.w = o[db][4 * i + 3] * inv;
+          *(float4*)(orow + db * 32 + 8 * i + 4 * hh) = w;
+        }
+      if (hh == 0) Lpart[prow] = lse;
+    }
+  }
+}
+
+// ---------------------------------------------------------------- launchers
+
+template <typename T, int D, bool CAUSAL, bool SPLIT>
+hipError_t launch_one(const FwdArgs& a, hipStream_t st) {
+  using C = ShortCfg<D>;
+  // K and V are addressed per head through 32-bit buffer offsets
+  if ((long long)(a.S_k + 4 * C::BN) * C::RB > 0x7fffffffLL) return hipErrorInvalidValue;
+  const int n_qt = (a.S_q + C::BM - 1) / C::BM;
+  const int n_work = a.B * a.H * n_qt * a.n_split;
+  hipLaunchKernelGGL((fwd_short_kernel<T, D, CAUSAL, SPLIT>), dim3(n_work), dim3(C::NT), 0, st,
+                     (const T*)a.q, (const T*)a.k, (const T*)a.v, (T*)a.o, a.lse, a.opart, a.lpart,
+                     a.B * a.H, a.S_q, a.S_k, n_qt, a.n_split, a.keys_per_split, a.c);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch_d(const FwdArgs& a, hipStream_t st) {
+  const bool split = a.n_split > 1;
+  if (a.causal) return split ? launch_one<T, D, true, true>(a, st) : launch_one<T, D, true, false>(a, st);
+  return split ? launch_one<T, D, false, true>(a, st) : launch_one<T, D, false, false>(a, st);
+}
+
+template <typename T>
+hipError_t launch_t(const FwdArgs& a, hipStream_t st) {
+  switch (a.D) {
+    case 64: return launch_d<T, 64>(a, st);
+    case 128: return launch_d<T, 128>(a, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+int short_keys_per_tile() { return ShortCfg<128>::BN; }
+int short_rows_per_block() { return ShortCfg<128>::BM; }
+
+hipError_t launch_fwd_short(const FwdArgs& a, hipStream_t st) {
+  if (a.dtype == 2) return launch_t<__bf16>(a, st);
+  return launch_t<_Float16>(a, st);
+}
+
+}  // namespace attn

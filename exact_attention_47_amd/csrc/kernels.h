@@ -27,6 +27,11 @@ hipError_t launch_fwd_mfma(const FwdArgs& a, hipStream_t st);
 int mfma_rows_per_block(int D);
 int mfma_keys_per_tile(int D);
 
+// short causal key ranges, D = 64 / 128 (two co-resident 4-wave workgroups per CU)
+hipError_t launch_fwd_short(const FwdArgs& a, hipStream_t st);
+int short_rows_per_block();
+int short_keys_per_tile();
+
 // head dimension 256 (called through launch_fwd_mfma)
 hipError_t launch_fwd_d256(const FwdArgs& a, hipStream_t st);
 int d256_keys_per_tile();
