@@ -81,3 +81,41 @@ def qkv(b, h, s_q, s_k, d, seed=0, dtype=torch.bfloat16, device="cpu", outliers=
     k = make((b, h, s_k, d), seed, TENSOR_K, dtype=dtype, device=device)
     v = make((b, h, s_k, d), seed, TENSOR_V, dtype=dtype, device=device)
     return q, k, v
+
+
+TENSOR_LENGTHS = 6
+
+
+def packed_qkv(lens_q, lens_k, h, d, seed=0, dtype=torch.bfloat16, device="cpu"):
+    """(Q, K, V, cu_q, cu_k) of a packed batch: Q [sum(lens_q), H, D], K and V [sum(lens_k), H, D].
+
+    Sequence b is drawn as its own chunk (its rows do not depend on the other
+    sequences' lengths); cu_* are int32 offsets (0, running totals) on ``device``.
+    """
+    lens_q = [int(x) for x in lens_q]
+    lens_k = [int(x) for x in lens_k]
+    if len(lens_q) != len(lens_k) or min(lens_q + lens_k) < 0:
+        raise ValueError("one non-negative query and key length per sequence")
+    out = []
+    for tid, lens in ((TENSOR_Q, lens_q), (TENSOR_K, lens_k), (TENSOR_V, lens_k)):
+        t = torch.empty((sum(lens), h, d), dtype=dtype, device=device)
+        row = 0
+        for b, n in enumerate(lens):
+            if n:
+                g = _gen(device, seed, tid, b)
+                t[row:row + n].copy_(torch.randn((n, h, d), generator=g, device=device, dtype=torch.float32).to(dtype))
+            row += n
+        out.append(t)
+    cu_q = torch.tensor(np.concatenate([[0], np.cumsum(lens_q)]), dtype=torch.int32, device=device)
+    cu_k = torch.tensor(np.concatenate([[0], np.cumsum(lens_k)]), dtype=torch.int32, device=device)
+    return (*out, cu_q, cu_k)
+
+
+def sequence_lengths(n_seq: int, total: int, seed: int, min_len: int = 1):
+    """``n_seq`` lengths >= ``min_len`` summing to ``total``: a uniform random split of the total."""
+    if n_seq < 1 or total < n_seq * min_len:
+        raise ValueError("total too small for the number of sequences")
+    g = _gen("cpu", seed, TENSOR_LENGTHS)
+    cuts = torch.randperm(total - n_seq * min_len + n_seq - 1, generator=g)[:n_seq - 1].sort().values
+    edges = [-1] + cuts.tolist() + [total - n_seq * min_len + n_seq - 1]
+    return [edges[i + 1] - edges[i] - 1 + min_len for i in range(n_seq)]

@@ -30,6 +30,7 @@ from .attention import (  # noqa: F401
     merge_partials,
     allowed_mask,
 )
+from .varlen import attention_varlen  # noqa: F401
 from .hadamard import sylvester, fwht, random_sign_hadamard  # noqa: F401
 from .fp8 import (  # noqa: F401
     E4M3_MAX,

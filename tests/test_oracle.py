@@ -416,3 +416,95 @@ def test_fp8_sim_p_rounding_is_a_small_perturbation():
     o1, _ = oracle.fp8_attention_sim(q, k, v, False, 0.125, "hadamard", sg, p_quant=True)
     e0, e1 = oracle.rmse(o0, ref), oracle.rmse(o1, ref)
     assert e0 <= e1 < 1.3 * e0
+
+
+# ---------------------------------------------------------------- packed (variable-length) batches
+
+def _packed(lens_q, lens_k, heads, d, seed):
+    rng = np.random.default_rng(seed)
+    cu_q = np.concatenate([[0], np.cumsum(lens_q)])
+    cu_k = np.concatenate([[0], np.cumsum(lens_k)])
+    q = rng.standard_normal((cu_q[-1], heads, d))
+    k = rng.standard_normal((cu_k[-1], heads, d))
+    v = rng.standard_normal((cu_k[-1], heads, d))
+    return q, k, v, cu_q, cu_k
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_varlen_single_sequence_equals_dense_definition(causal):
+    """One sequence: the packed oracle on [S, H, D] equals the dense one on [1, H, S, D]."""
+    q, k, v, cu_q, cu_k = _packed([37], [53], 3, 16, 1)
+    o, lse = oracle.attention_varlen(q, k, v, cu_q, cu_k, causal, 0.3)
+    od, lsed = oracle.attention(q.transpose(1, 0, 2)[None], k.transpose(1, 0, 2)[None],
+                                v.transpose(1, 0, 2)[None], causal, 0.3)
+    assert np.abs(o - od[0].transpose(1, 0, 2)).max() < TIGHT
+    assert np.abs(lse - lsed[0]).max() < TIGHT
+
+
+def test_varlen_equal_lengths_equal_batched_sdpa():
+    """Equal lengths: the packed batch is a [B, H, S, D] batch in another layout (torch SDPA, fp64)."""
+    B, S, H, D = 3, 24, 2, 8
+    q, k, v, cu_q, cu_k = _packed([S] * B, [S] * B, H, D, 2)
+    o, lse = oracle.attention_varlen(q, k, v, cu_q, cu_k, True, 1 / math.sqrt(D))
+    tq = torch.from_numpy(q.reshape(B, S, H, D).transpose(0, 2, 1, 3).copy())
+    tk = torch.from_numpy(k.reshape(B, S, H, D).transpose(0, 2, 1, 3).copy())
+    tv = torch.from_numpy(v.reshape(B, S, H, D).transpose(0, 2, 1, 3).copy())
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=True).numpy()
+    assert np.abs(o.reshape(B, S, H, D).transpose(0, 2, 1, 3) - ref).max() < TIGHT
+    s = (tq @ tk.transpose(-1, -2)).numpy() / math.sqrt(D)
+    s = np.where(np.tril(np.ones((S, S), dtype=bool)), s, -np.inf)
+    ref_lse = torch.logsumexp(torch.from_numpy(s), -1).numpy()        # [B, H, S]
+    assert np.abs(lse.reshape(H, B, S).transpose(1, 0, 2) - ref_lse).max() < TIGHT
+
+
+def test_varlen_sequences_are_independent_and_order_free():
+    """Changing one sequence leaves the others' outputs unchanged; reordering sequences reorders outputs."""
+    lens_q, lens_k = [5, 17, 9], [11, 17, 30]
+    q, k, v, cu_q, cu_k = _packed(lens_q, lens_k, 2, 8, 3)
+    o, lse = oracle.attention_varlen(q, k, v, cu_q, cu_k, True, 0.5)
+    k2, v2 = k.copy(), v.copy()
+    k2[cu_k[1]:cu_k[2]] += 3.0
+    v2[cu_k[1]:cu_k[2]] -= 1.0
+    o2, lse2 = oracle.attention_varlen(q, k2, v2, cu_q, cu_k, True, 0.5)
+    for b in (0, 2):
+        assert np.array_equal(o[cu_q[b]:cu_q[b + 1]], o2[cu_q[b]:cu_q[b + 1]])
+        assert np.array_equal(lse[:, cu_q[b]:cu_q[b + 1]], lse2[:, cu_q[b]:cu_q[b + 1]])
+    assert not np.allclose(o[cu_q[1]:cu_q[2]], o2[cu_q[1]:cu_q[2]])
+    order = [2, 0, 1]
+    rq = np.concatenate([q[cu_q[b]:cu_q[b + 1]] for b in order])
+    rk = np.concatenate([k[cu_k[b]:cu_k[b + 1]] for b in order])
+    rv = np.concatenate([v[cu_k[b]:cu_k[b + 1]] for b in order])
+    rcq = np.concatenate([[0], np.cumsum([lens_q[b] for b in order])])
+    rck = np.concatenate([[0], np.cumsum([lens_k[b] for b in order])])
+    ro, rlse = oracle.attention_varlen(rq, rk, rv, rcq, rck, True, 0.5)
+    assert np.array_equal(ro, np.concatenate([o[cu_q[b]:cu_q[b + 1]] for b in order]))
+    assert np.array_equal(rlse, np.concatenate([lse[:, cu_q[b]:cu_q[b + 1]] for b in order], axis=1))
+
+
+def test_varlen_causal_alignment_closed_form():
+    """Q = 0: every allowed key weighs the same, so LSE_i = ln(#allowed) and O_i = mean of the allowed V.
+
+    Per sequence, causal allows i + 1 + (S_k - S_q) keys (at most S_k, at least 0): the bottom-right
+    alignment, seen through the counts; rows with none get O = 0, LSE = -inf.
+    """
+    lens_q, lens_k = [6, 4, 3, 2], [9, 4, 0, 1]
+    q, k, v, cu_q, cu_k = _packed(lens_q, lens_k, 2, 4, 4)
+    q[:] = 0.0
+    o, lse = oracle.attention_varlen(q, k, v, cu_q, cu_k, True, 1.0)
+    for b, (sq, sk) in enumerate(zip(lens_q, lens_k)):
+        for i in range(sq):
+            n = min(sk, max(0, i + 1 + sk - sq))
+            row = cu_q[b] + i
+            if n == 0:
+                assert np.all(o[row] == 0.0) and np.all(lse[:, row] == -np.inf)
+            else:
+                assert np.abs(lse[:, row] - math.log(n)).max() < TIGHT
+                assert np.abs(o[row] - v[cu_k[b]:cu_k[b] + n].mean(axis=0)).max() < TIGHT
+
+
+def test_varlen_rejects_bad_offsets():
+    q, k, v, cu_q, cu_k = _packed([3, 4], [3, 4], 1, 4, 5)
+    with pytest.raises(ValueError):
+        oracle.attention_varlen(q, k, v, np.array([0, 5, 4]), cu_k, False, 1.0)
+    with pytest.raises(ValueError):
+        oracle.attention_varlen(q, k, v, cu_q, np.array([1, 3, 7]), False, 1.0)
