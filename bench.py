@@ -108,6 +108,24 @@ def decode_point(steps=10, warmup=3):
     return res
 
 
+def varlen_point(causal=True, steps=10, warmup=3):
+    """Packed batch: 8 sequences of random lengths (>= 256) summing to 16K tokens, H=16, D=128, bf16."""
+    lens = inputs.sequence_lengths(8, 16384, 0, 256)
+    H, D = 16, 128
+    q, k, v, cu_q, cu_k = inputs.packed_qkv(lens, lens, H, D, seed=0, device="cuda")
+    o = torch.empty_like(q)
+    lse = torch.empty((H, q.shape[0]), dtype=torch.float32, device="cuda")
+    mq = max(lens)
+    ms, _ = time_launches(lambda: attn.fwd_varlen(q, k, v, cu_q, cu_k, mq, mq, causal, 1 / math.sqrt(D),
+                                                  out=o, lse=lse, validate=False), steps, warmup)
+    fl = sum(flops(1, H, n, n, D, causal) for n in lens)
+    res = {"lens": lens, "H": H, "D": D, "causal": causal, "ms": round(ms, 4), "tflops": round(fl / ms / 1e9, 1),
+           "pct_peak": round(100 * fl / ms / 1e9 / PEAK_BF16, 1)}
+    del q, k, v, o, lse
+    torch.cuda.empty_cache()
+    return res
+
+
 def fp8_point(steps=10, warmup=3):
     """FP8 pipeline on the outlier workload: B=2, H=16, S=8K, D=128, non-causal."""
     B, H, S, D = 2, 16, 8192, 128
@@ -166,7 +184,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["fp8", "decode", "d256", "causal_sweep", "d64_sweep"], default=None,
+    ap.add_argument("--only", choices=["fp8", "decode", "d256", "causal_sweep", "d64_sweep", "varlen"],
+                    default=None,
                     help="run just this extra workload and print its JSON (for profiling one kernel family)")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="instead of the bench, run K plain device-to-device copies of this many bytes "
@@ -199,6 +218,7 @@ def main():
                                      for n in (512, 1024, 2048, 4096, 8192, 16384)],
             "d64_sweep": lambda: [bf16_point(16384 // n, 32, n, n, 64, False, steps=st, warmup=wu)
                                   for n in (512, 1024, 2048, 4096, 8192, 16384)],
+            "varlen": lambda: [varlen_point(c, steps=st, warmup=wu) for c in (True, False)],
         }
         print(json.dumps({"only": args.only, "result": runs[args.only]()}), flush=True)
         return
@@ -265,6 +285,7 @@ def main():
         extras["causal_d256_8k"] = bf16_point(2, 8, 8192, 8192, 256, True)
         extras["decode_32k"] = decode_point()
         extras["fp8_pipeline_8k"] = fp8_point()
+        extras["varlen_16k_tokens"] = [varlen_point(True), varlen_point(False)]
         out["extras"] = extras
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(B, H, S, D, causal)

@@ -42,6 +42,7 @@ _SIGS = {
     "hadamard_quant": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp]),
     "quant_per_tensor": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp]),
     "attn_fwd_fp8": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i, _i, _vp]),
+    "attn_fwd_varlen": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _f, _i, _vp]),
 }
 
 
@@ -135,6 +136,62 @@ def fwd(q, k, v, causal=False, scale=None, out=None, lse=None, num_splits=None, 
             workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
         wsz = 0 if workspace is None else workspace.numel() * workspace.element_size()
         _check("attn_fwd_ex", lib.attn_fwd_ex(*args, int(num_splits), _ptr(workspace), wsz, st))
+    return out, lse
+
+
+def fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q=None, max_seqlen_k=None, causal=False,
+               scale=None, out=None, lse=None, validate=True):
+    """O [total_q, H, D], LSE [H, total_q] for a packed batch of sequences.
+
+    ``q`` is [total_q, H, D], ``k``/``v`` are [total_k, H, D]; sequence b owns
+    rows ``cu_seqlens_q[b]:cu_seqlens_q[b+1]`` (int32 GPU tensors of B+1
+    entries). The kernel reads the offsets on the device and trusts them, so
+    with ``validate`` (the default) they are copied to the host once and
+    checked here; the maxima are taken from them when not given.
+    """
+    _need_gpu(q, k, v, cu_seqlens_q, cu_seqlens_k)
+    if q.dim() != 3 or k.dim() != 3 or v.dim() != 3:
+        raise ValueError("q, k, v must be [total, H, D]")
+    if not (q.dtype == k.dtype == v.dtype) or q.dtype not in (torch.float16, torch.bfloat16):
+        raise ValueError("q, k, v must share float16 or bfloat16")
+    total_q, H, D = q.shape
+    total_k = k.shape[0]
+    if tuple(k.shape) != (total_k, H, D) or tuple(v.shape) != (total_k, H, D):
+        raise ValueError("k and v must be [total_k, H, D] matching q")
+    if cu_seqlens_q.dtype != torch.int32 or cu_seqlens_k.dtype != torch.int32:
+        raise ValueError("cu_seqlens must be int32")
+    if cu_seqlens_q.dim() != 1 or cu_seqlens_q.shape != cu_seqlens_k.shape or cu_seqlens_q.numel() < 2:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must be 1-D with the same B+1 >= 2 entries")
+    B = cu_seqlens_q.numel() - 1
+    if validate or max_seqlen_q is None or max_seqlen_k is None:
+        cq, ck = cu_seqlens_q.cpu(), cu_seqlens_k.cpu()
+        for cu, total, name in ((cq, total_q, "q"), (ck, total_k, "k")):
+            if int(cu[0]) != 0 or int(cu[-1]) != total or bool((cu[1:] < cu[:-1]).any()):
+                raise ValueError(f"cu_seqlens_{name} must start at 0, not decrease and end at {total}")
+        lq, lk = int((cq[1:] - cq[:-1]).max()), int((ck[1:] - ck[:-1]).max())
+        if max_seqlen_q is None:
+            max_seqlen_q = lq
+        if max_seqlen_k is None:
+            max_seqlen_k = lk
+        if lq > max_seqlen_q or lk > max_seqlen_k:
+            raise ValueError("a sequence is longer than max_seqlen")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((H, total_q), dtype=torch.float32, device=q.device)
+    _need_gpu(out, lse)
+    if tuple(out.shape) != tuple(q.shape) or out.dtype != q.dtype or tuple(lse.shape) != (H, total_q) \
+            or lse.dtype != torch.float32:
+        raise ValueError("out must be like q and lse float32 [H, total_q]")
+    if total_q == 0:
+        return out, lse
+    st = _stream(q.device)
+    _check("attn_fwd_varlen", load().attn_fwd_varlen(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), B, H,
+        total_q, total_k, int(max_seqlen_q), int(max_seqlen_k), D, int(causal), float(scale), _DTYPE[q.dtype],
+        st))
     return out, lse
 
 

@@ -186,6 +186,51 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse
   return rc;
 }
 
+int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                    const int* cu_seqlens_q, const int* cu_seqlens_k, int B, int H, int total_q,
+                    int total_k, int max_seqlen_q, int max_seqlen_k, int D, int causal, float scale,
+                    int dtype, void* stream) {
+  int rc = ATTN_OK;
+  // (tensors of zero rows may be NULL)
+  if (((!q || !o || !lse) && total_q > 0) || ((!k || !v) && total_k > 0) || !cu_seqlens_q || !cu_seqlens_k)
+    rc = ATTN_ERR_INVALID_ARG;
+  else if (B <= 0 || H <= 0 || D <= 0 || total_q < 0 || total_k < 0 || max_seqlen_q < 0 ||
+           max_seqlen_k < 0 || max_seqlen_q > total_q || max_seqlen_k > total_k)
+    rc = ATTN_ERR_INVALID_ARG;
+  else if (dtype != ATTN_F32 && dtype != ATTN_F16 && dtype != ATTN_BF16) rc = ATTN_ERR_INVALID_ARG;
+  else if (causal != 0 && causal != 1) rc = ATTN_ERR_INVALID_ARG;
+  else if (!(scale > 0.0f) || !isfinite(scale)) rc = ATTN_ERR_INVALID_ARG;
+  else if (dtype == ATTN_F32 || (D != 64 && D != 128)) rc = ATTN_ERR_UNSUPPORTED;
+  else if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4) ||
+           !aligned(cu_seqlens_q, 4) || !aligned(cu_seqlens_k, 4))
+    rc = ATTN_ERR_MISALIGNED;
+  if (rc == ATTN_OK && total_q > 0 && max_seqlen_q > 0) {
+    const int bm = attn::mfma_rows_per_block(D);
+    const long long blocks = (long long)B * H * ((max_seqlen_q + bm - 1) / bm);
+    if (blocks > 0x7fffffffLL) rc = ATTN_ERR_UNSUPPORTED;
+  }
+  if (rc != ATTN_OK) {
+    say("attn_fwd_varlen", rc);
+    return rc;
+  }
+  if (total_q == 0 || max_seqlen_q == 0) return ATTN_OK;
+  attn::FwdArgs a;
+  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
+  a.B = B; a.H = H; a.S_q = max_seqlen_q; a.S_k = max_seqlen_k; a.D = D;
+  a.causal = causal; a.dtype = dtype;
+  a.n_split = 1; a.keys_per_split = 0;
+  a.c = scale * attn::kLog2e;
+  a.opart = nullptr; a.lpart = nullptr;
+  a.cu_q = cu_seqlens_q; a.cu_k = cu_seqlens_k; a.total_q = total_q;
+  const hipError_t e = attn::launch_fwd_varlen(a, (hipStream_t)stream);
+  if (e != hipSuccess) {
+    rc = e == hipErrorInvalidValue ? ATTN_ERR_UNSUPPORTED : ATTN_ERR_LAUNCH;
+    if (verbose()) fprintf(stderr, "[attn] varlen launch failed: %s\n", hipGetErrorString(e));
+    say("attn_fwd_varlen", rc);
+  }
+  return rc;
+}
+
 int hadamard_quant(const void* x, void* x8, float* scales, const signed char* signs, int B, int H,
                    int S, int D, int block_rows, int apply_hadamard, int in_dtype, void* stream) {
   if (!x || !x8 || !scales || !signs) return ATTN_ERR_INVALID_ARG;

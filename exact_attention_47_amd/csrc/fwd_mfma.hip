@@ -91,14 +91,16 @@ template <int D> __device__ __forceinline__ int v_swz(int r) { return D == 64 ? 
 constexpr float kTau = 8.0f;   // lazy-rescale threshold, log2 domain
 constexpr int kVmcnt0 = 0x0070 | 0x0F00;   // s_waitcnt vmcnt(0), other counters unconstrained
 
-template <typename T, int D, int BN, bool CAUSAL, bool SPLIT>
+template <typename T, int D, int BN, bool CAUSAL, bool SPLIT, bool VARLEN>
 __global__ void __launch_bounds__(512)
 __attribute__((amdgpu_waves_per_eu(2, 2)))
 fwd_mfma_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
                 T* __restrict__ O, float* __restrict__ LSE,
                 float* __restrict__ Opart, float* __restrict__ Lpart,
-                int BH, int S_q, int S_k, int n_qt, int n_split, int keys_per_split, float c)
+                int BH, int S_q_, int S_k_, int n_qt, int n_split, int keys_per_split, float c,
+                const int* __restrict__ cu_q, const int* __restrict__ cu_k, int H, int total_q)
 {
+  static_assert(!(VARLEN && SPLIT), "packed batches run unsplit");
   using C = FwdCfg<D, BN>;
   using M = Mma<T>;
   typedef typename M::frag frag;
@@ -112,16 +114,60 @@ fwd_mfma_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
   const int nn = lane & 31;        // query column owned by this lane
 
   // ---- which (b*h, q tile, split) this workgroup computes
-  const int n_work = BH * n_qt * n_split;
-  int work = xcd_swizzle(blockIdx.x, n_work);
-  const int split = work % n_split;
-  work /= n_split;
-  int qt = work % n_qt;
-  const int bh = work / n_qt;
-  if (CAUSAL) qt = n_qt - 1 - qt;  // heaviest query tiles first
+  int split, qt, bh;
+  if (!VARLEN) {
+    const int n_work = BH * n_qt * n_split;
+    int work = xcd_swizzle(blockIdx.x, n_work);
+    split = work % n_split;
+    work /= n_split;
+    qt = work % n_qt;
+    bh = work / n_qt;
+    if (CAUSAL) qt = n_qt - 1 - qt;  // heaviest query tiles first
+  } else {
+    // Packed batches: the sequences' lengths differ, so a contiguous share of
+    // the work per XCD (as above) would leave some XCDs with all the long
+    // sequences. Query tiles go out in descending order instead, all (b, h)
+    // at a time: high tiles exist only in long sequences, and causal tiles
+    // grow with the index, so the heaviest work starts first; the hardware
+    // deals consecutive workgroups to the 8 XCDs in turn, so (b, h) lands on
+    // XCD bh % 8 for every tile when B*H is a multiple of 8 (its K and V stay
+    // in one L2).
+    split = 0;
+    qt = n_qt - 1 - (int)(blockIdx.x / BH);
+    bh = blockIdx.x % BH;
+  }
 
   const int q0 = qt * C::BM;
   const int wr0 = q0 + wave * 32;              // first row of this wave
+
+  // ---- where this (b, h) lives. Dense: [B, H, S, D], rows D elements apart.
+  // Packed ([GN] "Weitere Optimierungen und kuenftige Integration" names
+  // variable-length sequences): [total, H, D], sequence b at rows
+  // cu[b] .. cu[b+1]-1, rows H*D elements apart; LSE is [H, total_q].
+  int S_q = S_q_, S_k = S_k_;
+  const int pitch = VARLEN ? H * D : D;        // elements between consecutive rows
+  const T *Qh, *Kh, *Vh;
+  T* Oh;
+  float* lseh;
+  if (VARLEN) {
+    const int b = bh / H, h = bh % H;
+    const int q_beg = cu_q[b], k_beg = cu_k[b];
+    S_q = cu_q[b + 1] - q_beg;
+    S_k = cu_k[b + 1] - k_beg;
+    if (q0 >= S_q) return;                     // whole workgroup: past this sequence's rows
+    Qh = Q + ((size_t)q_beg * H + h) * D;
+    Kh = K + ((size_t)k_beg * H + h) * D;
+    Vh = V + ((size_t)k_beg * H + h) * D;
+    Oh = O + ((size_t)q_beg * H + h) * D;
+    lseh = LSE + (size_t)h * total_q + q_beg;
+  } else {
+    Qh = Q + (size_t)bh * S_q * D;
+    Kh = K + (size_t)bh * S_k * D;
+    Vh = V + (size_t)bh * S_k * D;
+    Oh = O + (size_t)bh * S_q * D;
+    lseh = LSE + (size_t)bh * S_q;
+  }
+  const int RBg = pitch * (int)sizeof(T);      // bytes between consecutive rows in memory
   const int diag = S_k - S_q;                  // causal: key j allowed iff j <= i + diag
   int k_lo = 0, k_hi = S_k;
   if (SPLIT) {
@@ -132,11 +178,6 @@ fwd_mfma_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
   if (CAUSAL) k_end = min(k_end, q0 + C::BM - 1 + diag + 1);
   const int n_tiles = k_end > k_lo ? (k_end - k_lo + C::BN - 1) / C::BN : 0;
 
-  const size_t qoff = (size_t)bh * S_q * D;
-  const size_t koff = (size_t)bh * S_k * D;
-  const T* Qh = Q + qoff;
-  const T* Kh = K + koff;
-  const T* Vh = V + koff;
 
   // ---- Q^T fragments (B operand of S^T), kept in registers
   frag qf[C::DS];
@@ -145,7 +186,7 @@ fwd_mfma_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
 #pragma unroll
     for (int ds = 0; ds < C::DS; ds++) {
       if (q < S_q) {
-        qf[ds] = *(const frag*)(Qh + (size_t)q * D + ds * 16 + 8 * hh);
+        qf[ds] = *(const frag*)(Qh + (size_t)q * pitch + ds * 16 + 8 * hh);
       } else {
 #pragma unroll
         for (int e = 0; e < 8; e++) qf[ds][e] = (T)0.0f;
@@ -162,38 +203,40 @@ fwd_mfma_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
   // or 32 (D=64) between its instructions, which leaves both swizzles
   // unchanged, so its part of the offset is one constant and the rest (tile
   // row and 1 KiB block) is wave-uniform: no vector arithmetic per load.
-  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)Kh, (short)0, S_k * C::RB, 0x00020000);
-  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)Vh, (short)0, S_k * C::RB, 0x00020000);
+  // (packed rows are strided: the range ends after the last row's D elements)
+  const int kv_bytes = VARLEN ? (S_k > 0 ? (S_k - 1) * RBg + C::RB : 0) : S_k * C::RB;
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)Kh, (short)0, kv_bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)Vh, (short)0, kv_bytes, 0x00020000);
   int lane_k, lane_v;
   {
     const int rsub = (lane * 16) / C::RB;           // row within the wave instruction
     const int u = ((lane * 16) % C::RB) / 16;       // physical chunk within the row
     const int r = wave * C::RPI + rsub;             // first row; later rows differ by a multiple of 16
-    lane_k = rsub * C::RB + ((u ^ k_swz<D>(r)) * 16);
-    lane_v = rsub * C::RB + ((u ^ v_swz<D>(r)) * 16);
+    lane_k = rsub * RBg + ((u ^ k_swz<D>(r)) * 16);
+    lane_v = rsub * RBg + ((u ^ v_swz<D>(r)) * 16);
   }
   // (offsets and destinations go through locals: a target builtin with
   // template-dependent argument expressions is dropped from the host pass)
   auto issue_stage = [&](int s) {
     char* base = lds + (s & 1) * C::STAGE;
     if (s < n_tiles) {
-      const int row0 = (k_lo + s * C::BN) * C::RB;
+      const int row0 = k_lo + s * C::BN;
 #pragma unroll
       for (int i = 0; i < 2 * C::NI; i++) {
         const int blk = i * 4 + wave;                // 1 KiB block of the tile
         char* dst = base + blk * 1024;
-        const int soff = row0 + blk * 1024;
+        const int soff = (row0 + blk * C::RPI) * RBg;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (__attribute__((address_space(3))) void*)dst, 16, lane_k,
                                                  soff, 0, 0);
       }
     }
     if (s >= 1 && s - 1 < n_tiles) {
-      const int row0 = (k_lo + (s - 1) * C::BN) * C::RB;
+      const int row0 = k_lo + (s - 1) * C::BN;
 #pragma unroll
       for (int i = 0; i < 2 * C::NI; i++) {
         const int blk = i * 4 + wave;
         char* dst = base + C::TILE + blk * 1024;
-        const int soff = row0 + blk * 1024;
+        const int soff = (row0 + blk * C::RPI) * RBg;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (__attribute__((address_space(3))) void*)dst, 16, lane_v,
                                                  soff, 0, 0);
       }
@@ -379,7 +422,7 @@ fwd_mfma_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
   const float lse = has ? (m + __builtin_log2f(lt)) * kLn2 : kNegInf;
   if (q < S_q) {
     if (!SPLIT) {
-      T* orow = O + qoff + (size_t)q * D;
+      T* orow = Oh + (size_t)q * pitch;
 #pragma unroll
       for (int db = 0; db < C::DB; db++)
 #pragma unroll
@@ -390,7 +433,7 @@ fwd_mfma_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
           for (int j = 0; j < 4; j++) w[j] = (T)(o[db][4 * i + j] * inv);
           *(v4t*)(orow + db * 32 + 8 * i + 4 * hh) = w;
         }
-      if (hh == 0) LSE[(size_t)bh * S_q + q] = lse;
+      if (hh == 0) lseh[q] = lse;
     } else {
       const size_t prow = ((size_t)split * BH + bh) * S_q + q;
       float* orow = Opart + prow * D;
@@ -424,15 +467,18 @@ template <int D> struct Shape;
 template <> struct Shape<64> { static constexpr int BN = FWD_D64_BN; };
 template <> struct Shape<128> { static constexpr int BN = FWD_D128_BN; };
 
-template <typename T, int D, bool CAUSAL, bool SPLIT>
+template <typename T, int D, bool CAUSAL, bool SPLIT, bool VARLEN = false>
 static hipError_t launch_one(const FwdArgs& a, hipStream_t st) {
   using C = FwdCfg<D, Shape<D>::BN>;
-  if ((long long)(a.S_k + C::BN) * C::RB > 0x7fffffffLL) return hipErrorInvalidValue;   // 32-bit buffer offsets
+  // 32-bit buffer offsets (packed rows: S_k is the longest sequence's length)
+  const long long row_bytes = VARLEN ? (long long)a.H * C::RB : C::RB;
+  if ((long long)(a.S_k + C::BN) * row_bytes > 0x7fffffffLL) return hipErrorInvalidValue;
   const int n_qt = (a.S_q + C::BM - 1) / C::BM;
   const int n_work = a.B * a.H * n_qt * a.n_split;
-  hipLaunchKernelGGL((fwd_mfma_kernel<T, D, Shape<D>::BN, CAUSAL, SPLIT>), dim3(n_work), dim3(C::NT), 0, st,
-                     (const T*)a.q, (const T*)a.k, (const T*)a.v, (T*)a.o, a.lse, a.opart, a.lpart,
-                     a.B * a.H, a.S_q, a.S_k, n_qt, a.n_split, a.keys_per_split, a.c);
+  hipLaunchKernelGGL((fwd_mfma_kernel<T, D, Shape<D>::BN, CAUSAL, SPLIT, VARLEN>), dim3(n_work), dim3(C::NT), 0,
+                     st, (const T*)a.q, (const T*)a.k, (const T*)a.v, (T*)a.o, a.lse, a.opart, a.lpart,
+                     a.B * a.H, a.S_q, a.S_k, n_qt, a.n_split, a.keys_per_split, a.c, a.cu_q, a.cu_k, a.H,
+                     a.total_q);
   return hipGetLastError();
 }
 
@@ -456,6 +502,20 @@ int mfma_keys_per_tile(int D) {
   return D == 64 ? Shape<64>::BN : D == 128 ? Shape<128>::BN : d256_keys_per_tile();
 }
 int mfma_rows_per_block(int D) { (void)D; return 256; }
+
+template <typename T>
+static hipError_t launch_varlen_t(const FwdArgs& a, hipStream_t st) {
+  switch (a.D) {
+    case 64: return a.causal ? launch_one<T, 64, true, false, true>(a, st) : launch_one<T, 64, false, false, true>(a, st);
+    case 128: return a.causal ? launch_one<T, 128, true, false, true>(a, st) : launch_one<T, 128, false, false, true>(a, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_fwd_varlen(const FwdArgs& a, hipStream_t st) {
+  if (a.dtype == 2) return launch_varlen_t<__bf16>(a, st);
+  return launch_varlen_t<_Float16>(a, st);
+}
 
 hipError_t launch_fwd_mfma(const FwdArgs& a, hipStream_t st) {
   if (a.D == 256) return launch_fwd_d256(a, st);

@@ -20,12 +20,20 @@ struct FwdArgs {
   int n_split;         // >= 1
   int keys_per_split;  // multiple of the kernel's key tile
   float c;             // scale * log2(e)
+  // packed batches ([total, H, D] with cumulative sequence starts): S_q and
+  // S_k above are then the longest query / key sequence
+  const int* cu_q = nullptr;
+  const int* cu_k = nullptr;
+  int total_q = 0;
 };
 
 // bf16 / fp16 matrix-core kernel
 hipError_t launch_fwd_mfma(const FwdArgs& a, hipStream_t st);
 int mfma_rows_per_block(int D);
 int mfma_keys_per_tile(int D);
+
+// packed (variable-length) batches on the bf16 / fp16 kernel, D = 64 / 128
+hipError_t launch_fwd_varlen(const FwdArgs& a, hipStream_t st);
 
 // short causal key ranges, D = 64 / 128 (two co-resident 4-wave workgroups per CU)
 hipError_t launch_fwd_short(const FwdArgs& a, hipStream_t st);

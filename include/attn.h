@@ -99,6 +99,43 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse
                 int dtype, int num_splits, void* workspace, size_t workspace_bytes,
                 void* stream);
 
+/*
+ * attn_fwd_varlen -- attn_fwd over a packed batch of sequences of different
+ * lengths ([GN] "Weitere Optimierungen und kuenftige Integration" lists
+ * variable-length sequences among the full paper's optimizations; each
+ * sequence is attended exactly as attn_fwd would attend it alone).
+ *
+ *   q, o          [total_q, H, D], sequence b at rows cu_seqlens_q[b] ..
+ *                 cu_seqlens_q[b+1]-1 (element (t,h,d) at (t*H + h)*D + d)
+ *   k, v          [total_k, H, D], indexed by cu_seqlens_k the same way
+ *   lse           [H, total_q] float32 (natural-log logsumexp of the scaled
+ *                 scores of each row)
+ *   cu_seqlens_q, cu_seqlens_k
+ *                 device int32 arrays of B+1 entries: 0, then the running
+ *                 totals; nondecreasing, last entry total_q / total_k. They are
+ *                 read on the device only, so the library cannot check them:
+ *                 the caller guarantees this shape (and that no sequence is
+ *                 longer than max_seqlen_q / max_seqlen_k); otherwise the
+ *                 kernel reads and writes outside the tensors.
+ *   max_seqlen_q, max_seqlen_k
+ *                 upper bounds of the sequence lengths (they size the grid)
+ *   causal        per sequence, bottom-right aligned: key j of a sequence with
+ *                 S_q query and S_k key rows is allowed for its query i iff
+ *                 j <= i + S_k - S_q
+ *
+ * A query row with no allowed key (an empty key sequence, or causal rows
+ * above the diagonal when S_q > S_k) gets O = 0 and LSE = -inf. Empty query
+ * sequences write nothing. dtype is ATTN_BF16 or ATTN_F16 (ATTN_F32 and D =
+ * 256 return ATTN_ERR_UNSUPPORTED); D is 64 or 128. q, k, v, o must be
+ * 16-byte aligned, lse and the cu arrays 4-byte aligned; q, o, lse may be
+ * NULL when total_q = 0 and k, v when total_k = 0. total_q = 0 returns
+ * ATTN_OK without launching.
+ */
+int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                    const int* cu_seqlens_q, const int* cu_seqlens_k, int B, int H,
+                    int total_q, int total_k, int max_seqlen_q, int max_seqlen_k, int D,
+                    int causal, float scale, int dtype, void* stream);
+
 /* Bytes of workspace attn_fwd_ex needs for these sizes and split request
  * (0 when the effective split count is 1). num_splits = 0 means "automatic". */
 size_t attn_fwd_workspace_size(int B, int H, int S_q, int S_k, int D, int num_splits);

@@ -100,3 +100,38 @@ def test_split_plan():
     assert attn.workspace_size(1, 1, 4, 640, 128, 1) == 0
     n = attn.num_splits(64, 32, 1, 32768, 128)
     assert attn.workspace_size(64, 32, 1, 32768, 128) >= n * 64 * 32 * (128 + 1) * 4
+
+
+def varlen(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, cu_q=P, cu_k=P, B=2, H=2, total_q=300, total_k=400, max_q=200,
+             max_k=250, D=128, causal=0, scale=0.125, dtype=2)
+    a.update(kw)
+    return attn.load().attn_fwd_varlen(a["q"], a["k"], a["v"], a["o"], a["lse"], a["cu_q"], a["cu_k"], a["B"],
+                                       a["H"], a["total_q"], a["total_k"], a["max_q"], a["max_k"], a["D"],
+                                       a["causal"], ctypes.c_float(a["scale"]), a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(cu_q=None), attn.ERR_INVALID_ARG),
+    (dict(k=None), attn.ERR_INVALID_ARG),
+    (dict(B=0), attn.ERR_INVALID_ARG),
+    (dict(total_q=-1), attn.ERR_INVALID_ARG),
+    (dict(max_q=301), attn.ERR_INVALID_ARG),
+    (dict(max_k=-2), attn.ERR_INVALID_ARG),
+    (dict(dtype=9), attn.ERR_INVALID_ARG),
+    (dict(causal=3), attn.ERR_INVALID_ARG),
+    (dict(scale=-1.0), attn.ERR_INVALID_ARG),
+    (dict(dtype=0), attn.ERR_UNSUPPORTED),
+    (dict(D=256), attn.ERR_UNSUPPORTED),
+    (dict(D=96), attn.ERR_UNSUPPORTED),
+    (dict(q=P + 8), attn.ERR_MISALIGNED),
+    (dict(cu_k=P + 2), attn.ERR_MISALIGNED),
+])
+def test_varlen_validation_rejects(kw, code):
+    """Host-side checks of attn_fwd_varlen: each bad argument is refused before anything is enqueued."""
+    assert varlen(**kw) == code
+
+
+def test_varlen_empty_query_batch_is_a_no_op():
+    # zero query rows: nothing to compute, NULL q/o/lse allowed, nothing enqueued
+    assert varlen(q=None, o=None, lse=None, total_q=0, max_q=0) == attn.OK
