@@ -22,9 +22,9 @@
 // * Loads in the shadow of compute ([NL] "2. Minimalisatie van
 //   geheugenoperaties"). Stage t of a two-buffer LDS ring holds K(t) and
 //   V(t-1): exactly the operands of the matrix phase that reads it. Stage t+1
-//   is fetched with global_load_lds_dwordx4 (global memory straight into LDS,
-//   no registers) at the start of the step that reads stage t, and waited
-//   for just before the step's closing barrier.
+//   is fetched with buffer_load_dwordx4 ... lds (global memory straight into
+//   LDS, no registers) at the start of the step that reads stage t, and
+//   waited for just before the step's closing barrier.
 //
 // * Both GEMMs are transposed so that one lane owns one query row:
 //   S^T = K Q^T with v_mfma_f32_32x32x16 (A = K rows from LDS, B = Q^T from
