@@ -9,29 +9,32 @@
 // GEMM und Softmax durch Asynchronitaet"): the vector unit, not the matrix
 // core, bounds this kernel (about five vector instructions per score against
 // a quarter of a matrix instruction; on gfx950 an exponential holds the
-// vector unit about twice as long as an FMA, and the two do not overlap), so
-// its schedule keeps the vector unit fed from two waves per SIMD at all times.
+// vector unit about twice as long as an FMA, and the two do not overlap).
+// The schedule therefore aims at keeping the vector unit busy from as many
+// waves as the register file allows.
 //
 // * Work split: 4 waves x 32 query rows per workgroup, 64-key tiles (one K
 //   scale block and one k-step of the P V product each). Three LDS stages of
-//   16 KiB: two workgroups share a CU, one wave of each per SIMD.
+//   16 KiB and at most 168 VGPRs per lane: three workgroups share a CU, one
+//   wave of each per SIMD.
 //
-// * Overlap inside each wave ([GN] "Overlap innerhalb einer Warpgroup"): step
-//   t computes S(t+1) = K(t+1) Q^T (v_mfma_scale_f32_32x32x64_f8f6f4, unit
-//   scales) with the exponentials and E4M3 packing of tile t spread between
-//   its matrix instructions, then O += V(t)^T P(t)^T with the row maximum of
-//   tile t+1 in between. Each step is straight-line code with a scheduling
-//   barrier after every matrix instruction; masked tiles (key-range tail,
-//   causal diagonal) are a suffix of a wave's tiles and run in a second
-//   unrolled loop; scores past the range are -inf instead of skipped; a move
-//   of the row maximum is applied to O at the next step, after that tile's
-//   P V (still exact).
+// * Each wave runs its tiles in order: S(t) = K(t) Q^T
+//   (v_mfma_scale_f32_32x32x64_f8f6f4, unit scales), mask (a suffix of the
+//   wave's tiles: key-range tail, causal diagonal), softmax, E4M3 packing,
+//   then O += V(t)^T P(t)^T. The overlap of matrix and vector work that the
+//   pages build inside a warpgroup ([GN] "Overlap innerhalb einer
+//   Warpgroup") comes here from the three waves of a SIMD, which are at
+//   different points of their steps; with the software pipeline inside each
+//   wave the registers allowed only two waves per SIMD, and three plain waves
+//   measured 4-6 % faster.
 //
 // * Scores: s = scale * qs * ks * (q8 . k8), with qs the block scale of this
 //   wave's 32 rows and ks that of the tile's 64 keys; their product with
-//   log2(e) is one multiplier per tile, folded into the exp2 argument. P is
-//   rounded to E4M3 as p * 2^7 (the factor is added to the exponent for free)
-//   so small probabilities stay out of the subnormal range; the row sum l is
+//   log2(e) is one multiplier per tile, folded into the exp2 argument (the
+//   next tile's scale is fetched a step ahead with a vector load: a scalar
+//   load in flight would turn every LDS wait into a full one). P is rounded
+//   to E4M3 as p * 2^7 (the factor is added to the exponent for free) so
+//   small probabilities stay out of the subnormal range; the row sum l is
 //   accumulated from the unrounded p * 2^7, and the 2^7 cancels in
 //   O = acc * vs / l. The running maximum moves whenever a row exceeds it by
 //   more than 1.75 (log2), which keeps p * 2^7 <= 430 < 448; at each move the
@@ -47,9 +50,9 @@
 // * LDS: K and V tiles [64][128 bytes], 16-byte-chunk XOR swizzles chosen so
 //   that the K reads (16 lanes per LDS cycle over 16 rows) and the transposed
 //   V reads (32 lanes over 8 rows x 32 bytes) hit all 64 banks once. Stage
-//   j = {K(j), V(j-1)} lives in one of three separate __shared__ arrays (the
+//   j = {K(j), V(j)} lives in one of three separate __shared__ arrays (the
 //   compiler can then tell a direct load into one from a read of another;
-//   the loop is unrolled by three); stage t+3 is fetched with buffer loads at
+//   the loop is unrolled by three); stage t+2 is fetched with buffer loads at
 //   the start of step t and waited for at the end of step t+1.
 #include "common.h"
 #include "kernels.h"
@@ -92,7 +95,7 @@ template <int N> struct IC8 { static constexpr int value = N; };
 
 template <bool CAUSAL>
 __global__ void __launch_bounds__(NT8)
-__attribute__((amdgpu_waves_per_eu(2, 2)))
+__attribute__((amdgpu_waves_per_eu(3, 3)))
 fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ K8, const uint8_t* __restrict__ V8,
                const float* __restrict__ qs, const float* __restrict__ ks, const float* __restrict__ vs,
                __bf16* __restrict__ O, float* __restrict__ LSE, int BH, int S_q, int S_k, int n_qt, float c)
@@ -144,15 +147,10 @@ fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ K8, c
     }
   }
 
-  // stage j = K(j), V(j-1): every wave issues NI8 K and NI8 V instructions
-  // (1 KiB = 8 rows each), buffer loads on per-head resources; rows outside
-  // K/V read zeros, so every stage issues the same number of instructions
+  // stage j = K(j), V(j): every wave issues NI8 K and NI8 V loads (1 KiB =
+  // 8 rows each) on per-head buffer resources; rows past the end read zeros
   const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)Kh, (short)0, S_k * D8, 0x00020000);
   const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)Vh, (short)0, S_k * D8, 0x00020000);
-  // lane part of each load's offset (lane-constant: the swizzle repeats every
-  // 16 rows and every load covers 8 rows at a multiple of 8) plus a
-  // wave-uniform stage offset; stage 0 has no V tile (its V loads would
-  // start before the buffer) and is waited for in full before the loop
   int lane_k[NI8], lane_v[NI8];
 #pragma unroll
   for (int i = 0; i < NI8; i++) {
@@ -163,21 +161,14 @@ fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ K8, c
   // (offsets and destinations go through locals: a target builtin with
   // template-dependent argument expressions is dropped from the host pass)
   auto issue_stage = [&](int j, char* base) {
-    const int soff_k = j * TILE8;
-    const int soff_v = (j - 1) * TILE8;
+    const int soff = j * TILE8;
 #pragma unroll
     for (int i = 0; i < NI8; i++) {
       char* kdst = base + (i * NW8 + wave) * 1024;
-      const int lk = lane_k[i];
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (__attribute__((address_space(3))) void*)kdst, 16, lk, soff_k, 0, 0);
-    }
-    if (j >= 1) {
-#pragma unroll
-      for (int i = 0; i < NI8; i++) {
-        char* vdst = base + TILE8 + (i * NW8 + wave) * 1024;
-        const int lv = lane_v[i];
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (__attribute__((address_space(3))) void*)vdst, 16, lv, soff_v, 0, 0);
-      }
+      char* vdst = base + TILE8 + (i * NW8 + wave) * 1024;
+      const int lk = lane_k[i], lv = lane_v[i];
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (__attribute__((address_space(3))) void*)kdst, 16, lk, soff, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (__attribute__((address_space(3))) void*)vdst, 16, lv, soff, 0, 0);
     }
   };
 
@@ -201,131 +192,15 @@ fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ K8, c
   for (int db = 0; db < DB8; db++)
 #pragma unroll
     for (int e = 0; e < 16; e++) o[db][e] = 0.0f;
-  v16f sacc[3][KB8];               // scores of tiles j, j+1 (index j % 3)
-#pragma unroll
-  for (int kb = 0; kb < KB8; kb++)
-#pragma unroll
-    for (int e = 0; e < 16; e++) sacc[2][kb][e] = kNegInf;   // "tile -1"
-  v8i pf;
-  float m = kNegInf, l = 0.0f, rf = 0.0f, alpha = 1.0f, xmax = kNegInf;
-  bool resc = false;
+  float m = kNegInf, l = 0.0f, rf = 0.0f;
 
-  auto tile_active = [&](int t) { return !CAUSAL || t * BN8 <= wr0 + 31 + diag; };
-  auto tile_scale = [&](int t) { return c_q * ksh[min(t * BN8, S_k - 1) / 64]; };
-  float cs_cur = 1.0f, cs_nxt = 1.0f;        // scales of the current and next tile
   const __amdgpu_buffer_rsrc_t ksrs = __builtin_amdgcn_make_buffer_rsrc((void*)ksh, (short)0, nk_blk * 4, 0x00020000);
   auto tile_scale_v = [&](int t) {
     const int off = (min(t * BN8, S_k - 1) / 64) * 4;
     return c_q * __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ksrs, off, 0, 0));
   };
+  float cs_cur = c_q * ksh[0];
 
-  auto mask = [&](v16f* sn, int t) {
-    const int key0 = t * BN8;
-    const int q = wr0 + nn;
-#pragma unroll
-    for (int kb = 0; kb < KB8; kb++)
-#pragma unroll
-      for (int i = 0; i < 4; i++)
-#pragma unroll
-        for (int jx = 0; jx < 4; jx++) {
-          const int key = key0 + kb * 32 + 8 * i + 4 * hh + jx;
-          const bool ok = key < S_k && (!CAUSAL || key <= q + diag);
-          if (!ok) sn[kb][4 * i + jx] = kNegInf;
-        }
-  };
-  // row maximum of a new tile: decide whether the reference moves (applied to
-  // O and l once the previous tile's P V is in)
-  auto maxdec = [&] {
-    const float x = xmax;
-    resc = __any(x > m + kTau8);
-    if (resc) {
-      const float mnew = fmaxf(m, x);
-      const float r = mnew == kNegInf ? 0.0f : mnew;
-      alpha = fast_exp2(m - r);            // 0 when m was -inf
-      m = mnew;
-      rf = r;
-    }
-  };
-
-  // S(t+1)^T = K Q^T (four 32x32x64 steps: k2-major within each 32-key block)
-  // with the exponentials and E4M3 packing of tile t spread over the steps
-  constexpr int LA = 2;
-  auto sblock = [&](const char* st, v16f* sd, const v16f* sc, float cc) {
-    constexpr int NS = KB8 * 2;
-    constexpr int EPS = 16 * KB8 / NS;           // exponentials per step (8)
-    auto load = [&](int j) {
-      const int kb = j / 2, k2 = j % 2;
-      const char* kp = st + kb * 32 * D8;
-      const uint4 lo = *(const uint4*)(kp + k_rd[2 * k2]);
-      const uint4 hi = *(const uint4*)(kp + k_rd[2 * k2 + 1]);
-      return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-    };
-    v8i ring[LA + 1];
-#pragma unroll
-    for (int j = 0; j < LA; j++) ring[j] = load(j);
-    const float nref = -(rf - kPShift8);         // p * 2^7 = 2^(s*cc - rf + 7)
-#pragma unroll
-    for (int j = 0; j < NS; j++) {
-      if (j + LA < NS) ring[(j + LA) % (LA + 1)] = load(j + LA);
-      const int kb = j / 2, k2 = j % 2;
-      if (k2 == 0) {
-        const v16f zero = {};
-        sd[kb] = mma8(ring[j % (LA + 1)], qf[0], zero);
-      } else {
-        sd[kb] = mma8(ring[j % (LA + 1)], qf[1], sd[kb]);
-      }
-      // slots 4*q4 .. 4*q4+3 of block b go to word 4*b + q4 of P^T; the
-      // packed words and the row sum are written in place each step, which
-      // keeps this step's exponentials in this step (values only used at the
-      // end would be sunk past the scheduling barriers)
-#pragma unroll
-      for (int u = 0; u < EPS / 4; u++) {
-        const int quad = j * (EPS / 4) + u, b = quad / 4, q4 = quad % 4;
-        float p[4];
-#pragma unroll
-        for (int e = 0; e < 4; e++) {
-          p[e] = fast_exp2(__builtin_fmaf(sc[b][4 * q4 + e], cc, nref));
-          l += p[e];
-        }
-        pf[4 * b + q4] = (int)pack_fp8(p[0], p[1], p[2], p[3]);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
-  // O^T += V(t)^T P(t)^T (four 32x32x64 steps, one per 32-row block of O^T)
-  // with the row maximum of tile t+1 spread over the steps
-  auto pblock = [&](auto do_m, const char* st, const v16f* sn, float cn) {
-    constexpr bool DM = decltype(do_m)::value;
-    constexpr int MPS = 16 * KB8 / DB8;          // score elements per step (8)
-    const char* vl = st + TILE8;
-    auto load = [&](int db) {
-      v2i part[4];
-#pragma unroll
-      for (int p = 0; p < 4; p++) {
-        const int row0 = 32 * (p >> 1) + 16 * (p & 1);
-        part[p] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(vl + v_rd[db] + row0 * D8));
-      }
-      return v8i{part[0][0], part[0][1], part[1][0], part[1][1], part[2][0], part[2][1], part[3][0], part[3][1]};
-    };
-    v8i ring[LA + 1];
-#pragma unroll
-    for (int j = 0; j < LA; j++) ring[j] = load(j);
-    if (DM) xmax = kNegInf;
-#pragma unroll
-    for (int db = 0; db < DB8; db++) {
-      if (db + LA < DB8) ring[(db + LA) % (LA + 1)] = load(db + LA);
-      o[db] = mma8(ring[db % (LA + 1)], pf, o[db]);
-      if (DM) {                                  // (in place, like the row sum)
-#pragma unroll
-        for (int u = 0; u < MPS; u++) {
-          const int idx = db * MPS + u;
-          xmax = fmaxf(xmax, sn[idx / 16][idx % 16]);
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    if (DM) xmax = pair_max(xmax) * cn;
-  };
   auto barrier = [] {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
@@ -334,70 +209,120 @@ fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ K8, c
     asm volatile("" ::: "memory");
   };
 
-  // One step t (-1 <= t < n_tiles): stage t+1 (K(t+1), V(t)) is read from
-  // buffer (t+1) % 3 while stage t+3 is fetched into buffer t % 3.
+  // One step per tile t: S(t) = K(t) Q^T, softmax of tile t, O += V(t)^T P(t).
+  // The wave runs them in order; the three waves per SIMD (one of each of the
+  // CU's three workgroups) overlap one another's matrix and vector work.
   auto step = [&](auto bi, auto masked, int t) {
     constexpr int B = decltype(bi)::value;
     constexpr bool MASKED = decltype(masked)::value;
-    char* dbuf = B == 0 ? st0 : B == 1 ? st1 : st2;
-    const char* rbuf = B == 0 ? st1 : B == 1 ? st2 : st0;
-    v16f* scur = sacc[B];
-    v16f* snx = sacc[(B + 1) % 3];
-    // tile scales: loaded one step ahead as vector loads before the stage's
-    // loads (complete at this step's final wait), so that no scalar load is
-    // in flight while the step waits for its LDS reads: scalar and LDS loads
-    // share one counter, and a pending scalar load makes every wait a full one
-    const float c_cur = cs_cur, c_nxt = cs_nxt;
+    const char* rbuf = B == 0 ? st0 : B == 1 ? st1 : st2;
+    char* dbuf = B == 0 ? st2 : B == 1 ? st0 : st1;    // buffer (t + 2) % 3
+    const float cc = cs_cur;
     barrier();
-    const float c_pre = tile_scale_v(t + 2);
-    issue_stage(t + 3, dbuf);
-    if (resc) {
+    const float c_nx = tile_scale_v(t + 1);
+    issue_stage(t + 2, dbuf);
+    // S^T = K Q^T: four 32x32x64 steps (k2-major within each 32-key block)
+    v16f s[KB8];
+    {
+      auto load = [&](int j) {
+        const int kb = j / 2, k2 = j % 2;
+        const char* kp = rbuf + kb * 32 * D8;
+        const uint4 lo = *(const uint4*)(kp + k_rd[2 * k2]);
+        const uint4 hi = *(const uint4*)(kp + k_rd[2 * k2 + 1]);
+        return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      };
+      v8i ring[2];
+      ring[0] = load(0);
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        if (j + 1 < 4) ring[(j + 1) & 1] = load(j + 1);
+        const int kb = j / 2, k2 = j % 2;
+        if (k2 == 0) {
+          const v16f zero = {};
+          s[kb] = mma8(ring[j & 1], qf[0], zero);
+        } else {
+          s[kb] = mma8(ring[j & 1], qf[1], s[kb]);
+        }
+      }
+    }
+    if (MASKED) {
+      const int key0 = t * BN8;
+      const int q = wr0 + nn;
+#pragma unroll
+      for (int kb = 0; kb < KB8; kb++)
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+#pragma unroll
+          for (int jx = 0; jx < 4; jx++) {
+            const int key = key0 + kb * 32 + 8 * i + 4 * hh + jx;
+            const bool ok = key < S_k && (!CAUSAL || key <= q + diag);
+            if (!ok) s[kb][4 * i + jx] = kNegInf;
+          }
+    }
+    float x = kNegInf;
+#pragma unroll
+    for (int kb = 0; kb < KB8; kb++)
+#pragma unroll
+      for (int e = 0; e < 16; e++) x = fmaxf(x, s[kb][e]);
+    x = pair_max(x) * cc;
+    if (__any(x > m + kTau8)) {
+      const float mnew = fmaxf(m, x);
+      const float r = mnew == kNegInf ? 0.0f : mnew;
+      const float alpha = fast_exp2(m - r);      // 0 when m was -inf
+      m = mnew;
+      rf = r;
       l *= alpha;
 #pragma unroll
       for (int db = 0; db < DB8; db++)
 #pragma unroll
         for (int e = 0; e < 16; e++) o[db][e] *= alpha;
     }
-    sblock(rbuf, snx, scur, c_cur);
-    if (MASKED) {
-      mask(snx, t + 1);
-      pblock(IC8<0>(), rbuf, snx, c_nxt);
-      float x = kNegInf;
+    const float nref = kPShift8 - rf;            // p * 2^7 = 2^(s*cc - rf + 7)
+    v8i pf;
 #pragma unroll
-      for (int kb = 0; kb < KB8; kb++)
+    for (int quad = 0; quad < 8; quad++) {
+      const int b = quad / 4, q4 = quad % 4;
+      float p[4];
 #pragma unroll
-        for (int e = 0; e < 16; e++) x = fmaxf(x, snx[kb][e]);
-      xmax = pair_max(x) * c_nxt;
-    } else {
-      pblock(IC8<1>(), rbuf, snx, c_nxt);
+      for (int e = 0; e < 4; e++) {
+        p[e] = fast_exp2(__builtin_fmaf(s[b][4 * q4 + e], cc, nref));
+        l += p[e];
+      }
+      pf[quad] = (int)pack_fp8(p[0], p[1], p[2], p[3]);
     }
-    maxdec();
-    cs_cur = c_nxt;
-    cs_nxt = c_pre;
-    __builtin_amdgcn_s_waitcnt(0x0070 | 0x0F00 | (2 * NI8));   // stage t+2 complete
+    // O^T += V^T P^T: four 32x32x64 steps, one per 32-row block of O^T
+    {
+      const char* vl = rbuf + TILE8;
+      auto load = [&](int db) {
+        v2i part[4];
+#pragma unroll
+        for (int p = 0; p < 4; p++) {
+          const int row0 = 32 * (p >> 1) + 16 * (p & 1);
+          part[p] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(vl + v_rd[db] + row0 * D8));
+        }
+        return v8i{part[0][0], part[0][1], part[1][0], part[1][1], part[2][0], part[2][1], part[3][0], part[3][1]};
+      };
+      v8i ring[2];
+      ring[0] = load(0);
+#pragma unroll
+      for (int db = 0; db < DB8; db++) {
+        if (db + 1 < DB8) ring[(db + 1) & 1] = load(db + 1);
+        o[db] = mma8(ring[db & 1], pf, o[db]);
+      }
+    }
+    cs_cur = c_nx;
+    __builtin_amdgcn_s_waitcnt(0x0070 | 0x0F00 | (2 * NI8 + 1));   // stage t+1 complete
   };
 
-  // steps from t = -1 to the wave's last tile with an allowed key (see the
-  // main kernel's schedule notes); then only barriers and loads
   if (n_tiles > 0) {
     int t_last = n_tiles - 1;
     if (CAUSAL) {
       const int lim = wr0 + 31 + diag;
       t_last = lim < 0 ? -1 : min(t_last, lim / BN8);
     }
-    cs_cur = tile_scale(0);
-    cs_nxt = tile_scale(0);
-    {
-      // stage 0 holds no V tile; the first step multiplies its zero
-      // probabilities with that part of the buffer, which must not be NaN
-      uint4* vz = (uint4*)(st0 + TILE8);
-#pragma unroll
-      for (int i = 0; i < TILE8 / (NT8 * 16); i++) vz[i * NT8 + tid] = uint4{0, 0, 0, 0};
-    }
     issue_stage(0, st0);
     issue_stage(1, st1);
-    __builtin_amdgcn_s_waitcnt(0x0070 | 0x0F00);
-    __syncthreads();
+    __builtin_amdgcn_s_waitcnt(0x0070 | 0x0F00 | (2 * NI8));      // stage 0 complete
     int u_mask = S_k / BN8;                      // tiles that need no mask for any row of the wave
     if (CAUSAL) {
       const int lim2 = wr0 + diag + 1;
@@ -405,34 +330,27 @@ fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ K8, c
     }
     const IC8<0> P;
     const IC8<1> Mk;
-    int t = -1;
-    const int t_plain = min(t_last, u_mask - 2);
-    for (; t + 2 <= t_plain; t += 3) {
-      step(IC8<2>(), P, t);
-      step(IC8<0>(), P, t + 1);
-      step(IC8<1>(), P, t + 2);
+    int t = 0;
+    const int t_plain = min(t_last + 1, u_mask);  // tiles before this one need no mask
+    for (; t + 2 < t_plain; t += 3) {
+      step(IC8<0>(), P, t);
+      step(IC8<1>(), P, t + 1);
+      step(IC8<2>(), P, t + 2);
     }
     for (; t + 2 <= t_last; t += 3) {
-      step(IC8<2>(), Mk, t);
-      step(IC8<0>(), Mk, t + 1);
-      step(IC8<1>(), Mk, t + 2);
+      step(IC8<0>(), Mk, t);
+      step(IC8<1>(), Mk, t + 1);
+      step(IC8<2>(), Mk, t + 2);
     }
-    if (t <= t_last) { step(IC8<2>(), Mk, t); t++; }
     if (t <= t_last) { step(IC8<0>(), Mk, t); t++; }
-    for (; t < n_tiles; t++) {
-      const int bsel = (t + 3) % 3;
+    if (t <= t_last) { step(IC8<1>(), Mk, t); t++; }
+    for (; t < n_tiles; t++) {                   // the wave is done: keep the barriers and loads going
+      const int bsel = (t + 2) % 3;
       barrier();
-      issue_stage(t + 3, bsel == 0 ? st0 : bsel == 1 ? st1 : st2);
+      issue_stage(t + 2, bsel == 0 ? st0 : bsel == 1 ? st1 : st2);
       __builtin_amdgcn_s_waitcnt(0x0070 | 0x0F00 | (2 * NI8));
     }
     __builtin_amdgcn_s_waitcnt(0x0070 | 0x0F00);
-    if (resc) {                    // a reference change not yet applied (cannot happen: the
-      l *= alpha;                  // last scores a wave looks at are fully masked)
-#pragma unroll
-      for (int db = 0; db < DB8; db++)
-#pragma unroll
-        for (int e = 0; e < 16; e++) o[db][e] *= alpha;
-    }
   }
 
   // epilogue: O = acc * vs / l (the 2^7 of p cancels), LSE = ln2 * (m + log2 l - 7)
