@@ -56,12 +56,18 @@ Plan plan_splits(int dtype, int B, int H, int S_q, int S_k, int D, int req) {
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// Causal D = 128 attention over at most 2048 keys runs on the short-range
-// kernel (measured faster there: two workgroups per CU hide the start-up of
-// each other's few tiles); everything else on the main kernel. Requested
-// splits always go to the main kernel, whose key tile the split plan uses.
+// Short key ranges run on the short-range kernel (three or four small
+// workgroups per CU hide one another's start-up and memory waits), long ones
+// on the main kernel. Crossovers measured on the sweeps: D = 64 up to 4096
+// keys (+33 % at 512, +2 % at 4096, -1 % at 8192), D = 128 causal up to 2048
+// (+14 % at 512, -10 % at 4096), D = 128 non-causal up to 1024 (+16 % at 512,
+// -2 % at 2048). Requested splits always go to the main kernel, whose key
+// tile the split plan uses.
 bool use_short_kernel(int D, int causal, int S_k, int n_split) {
-  return D == 128 && causal && S_k <= 2048 && n_split == 1;
+  if (n_split != 1) return false;
+  if (D == 64) return S_k <= 4096;
+  if (D == 128) return S_k <= (causal ? 2048 : 1024);
+  return false;
 }
 
 size_t ws_bytes(const Plan& p, int B, int H, int S_q, int D) {

@@ -1,5 +1,6 @@
-// Fused exact attention forward pass for short causal sequences (bf16 / fp16,
-// D = 64 / 128): two co-resident workgroups per CU, each wave software-pipelined.
+// Fused exact attention forward pass for short key ranges (bf16 / fp16,
+// D = 64 / 128): three or four small workgroups per CU, each wave running its
+// tiles in order.
 //
 // Same method as the main kernel (O = softmax(scale Q K^T [+ causal]) V and
 // the row logsumexp by tiles with online softmax rescaling, [NL]
@@ -11,22 +12,25 @@
 // exposed:
 //
 // * 4 waves x 32 query rows per workgroup and 32-key tiles, so three LDS
-//   stages take 48 KiB and two workgroups fit on a CU (204 VGPRs per lane,
-//   one wave of each per SIMD): while one waits on memory the other computes.
+//   stages take 48 KiB (D = 128) or 24 KiB (D = 64). Each wave keeps only one
+//   tile's scores and probabilities live (at most 168 VGPRs at D = 128, 112 at
+//   D = 64), so three (D = 128) or four (D = 64) workgroups share a CU: one
+//   wave of each per SIMD.
 //
-// * Overlap inside each wave ([GN] "Overlap innerhalb einer Warpgroup"):
-//   step t computes S(t+1) = K(t+1) Q^T with the exponentials of tile t spread
-//   between its matrix instructions, then O += V(t)^T P(t)^T with the row
-//   maximum of tile t+1 in between. Each step is straight-line code with a
-//   scheduling barrier per matrix instruction: tiles that need a mask (the
-//   key-range tail, the causal diagonal) are always a suffix of a wave's
-//   tiles and run in a second unrolled loop; scores past the range are -inf
-//   instead of skipped; a row-maximum increase is applied to O at the next
-//   step, after that tile's P V (still exact).
+// * Each wave runs its tiles in order: S(t) = K(t) Q^T, mask (tiles that
+//   need one, the key-range tail and the causal diagonal, are a suffix of a
+//   wave's tiles and run in a second unrolled loop), online softmax, P(t) to
+//   matrix fragments, O += V(t)^T P(t)^T. The overlap of matrix and vector
+//   work ([GN] "Overlap innerhalb einer Warpgroup") comes from the other
+//   waves of the SIMD, which are at other points of their steps. A software
+//   pipeline inside each wave (exponentials of tile t between the MFMAs of
+//   tile t+1) needs two tiles' scores live and so allowed only two waves per
+//   SIMD; the plain order with three or four waves measured 7-33 % faster on
+//   these ranges.
 //
-// * Stage j = {K(j), V(j-1)} lives in one of three separate __shared__ arrays
+// * Stage j = {K(j), V(j)} lives in one of three separate __shared__ arrays
 //   (so the compiler can tell the direct load into one from the reads of
-//   another; the loop is unrolled by three). Stage t+3 is fetched with buffer
+//   another; the loop is unrolled by three). Stage t+2 is fetched with buffer
 //   loads into the array that step t-1 finished with, and waited for at the
 //   end of step t+1.
 #include "common.h"
@@ -64,7 +68,7 @@ struct ShortCfg {
   static constexpr int DB = D / 32;             // 32-wide column blocks of O^T
   static constexpr int RB = 2 * D;              // bytes per K/V row
   static constexpr int TILE = BN * RB;          // bytes per K or V tile
-  static constexpr int STAGE = 2 * TILE;        // K(j) then V(j-1)
+  static constexpr int STAGE = 2 * TILE;        // K(j) then V(j)
   static constexpr int NI = TILE / (NT * 16);   // direct-load instructions per thread per tile
   static constexpr int RPI = 1024 / RB;         // rows written by one wave instruction
   static_assert(TILE % (NT * 16) == 0, "tile must split evenly into 1 KiB wave loads");
@@ -76,27 +80,11 @@ template <int D> __device__ __forceinline__ int v_swz(int r) { return D == 64 ? 
 
 constexpr float kTau = 8.0f;   // lazy-rescale threshold, log2 domain
 
-// scheduling groups (instruction classes of __builtin_amdgcn_sched_group_barrier)
-#define SGB(mask, n) __builtin_amdgcn_sched_group_barrier(mask, n, 0)
-constexpr int kMFMA = 0x008, kVALU = 0x002 | 0x400, kDSR = 0x100;
-#ifndef LA_S
-#define LA_S 3
-#endif
-#ifndef LA_P
-#define LA_P 3
-#endif
-#ifndef VPS
-#define VPS 7
-#endif
-#ifndef VPP
-#define VPP 2
-#endif
-
 template <int N> struct IC { static constexpr int value = N; };
 
 template <typename T, int D, bool CAUSAL, bool SPLIT>
 __global__ void __launch_bounds__(256)
-__attribute__((amdgpu_waves_per_eu(2, 2)))
+__attribute__((amdgpu_waves_per_eu(D == 64 ? 4 : 3, D == 64 ? 4 : 3)))
 fwd_short_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
                 T* __restrict__ O, float* __restrict__ LSE,
                 float* __restrict__ Opart, float* __restrict__ Lpart,
@@ -159,7 +147,7 @@ fwd_short_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __re
     }
   }
 
-  // ---- direct global -> LDS loads: stage j = K(j) and V(j-1). Every wave
+  // ---- direct global -> LDS loads: stage j = K(j) and V(j). Every wave
   // issues its share (NI instructions per tile, 1 KiB each, lane i landing at
   // byte 16*i and fetching the logical chunk the swizzle stores there), as
   // buffer loads on per-head resources: rows outside K/V read zeros (their
@@ -172,13 +160,13 @@ fwd_short_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __re
   // (offsets and destinations go through locals: a target builtin with
   // template-dependent argument expressions is dropped from the host pass)
   auto issue_stage = [&](int j, char* base) {
-    const int krow0 = k_lo + j * C::BN;               // may be negative or past the end: reads 0
+    const int krow0 = k_lo + j * C::BN;               // past the end: reads 0
 #pragma unroll
     for (int i = 0; i < C::NI; i++) {
       const int blk = i * C::NW + wave;
       const int r = blk * C::RPI + dma_rsub;
       const int koff = (krow0 + r) * C::RB + ((dma_u ^ k_swz<D>(r)) * 16);
-      const int voff = (krow0 - C::BN + r) * C::RB + ((dma_u ^ v_swz<D>(r)) * 16);
+      const int voff = (krow0 + r) * C::RB + ((dma_u ^ v_swz<D>(r)) * 16);
       char* kdst = base + blk * 1024;
       char* vdst = base + C::TILE + blk * 1024;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (__attribute__((address_space(3))) void*)kdst, 16, koff, 0, 0, 0);
@@ -206,20 +194,49 @@ fwd_short_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __re
   for (int db = 0; db < C::DB; db++)
 #pragma unroll
     for (int e = 0; e < 16; e++) o[db][e] = 0.0f;
-  v16f sacc[3][C::KB];             // scores of tiles j, j+1 (index j % 3)
-#pragma unroll
-  for (int kb = 0; kb < C::KB; kb++)
-#pragma unroll
-    for (int e = 0; e < 16; e++) sacc[2][kb][e] = kNegInf;   // "tile -1"
-  frag pf[C::KB][2];
-  float m = kNegInf, l = 0.0f, rf = 0.0f, alpha = 1.0f;
-  bool resc = false;
+  float m = kNegInf, l = 0.0f;
 
-  auto tile_active = [&](int t) { return !CAUSAL || k_lo + t * C::BN <= wr0 + 31 + diag; };
+  auto barrier = [] {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+  };
 
-  auto mask = [&](v16f* sn, int t) {
-    const int key0 = k_lo + t * C::BN;
+  // One step per tile t, in order: S(t) = K(t) Q^T, mask, online softmax,
+  // P(t) -> fragments, O += V(t)^T P(t). Stage t (K(t), V(t)) is read from
+  // buffer t % 3 while stage t+2 is fetched into buffer (t+2) % 3.
+  auto step = [&](auto bi, auto masked, int t) {
+    constexpr int B = decltype(bi)::value;
+    constexpr bool MASKED = decltype(masked)::value;
+    const char* rbuf = B == 0 ? st0 : B == 1 ? st1 : st2;
+    char* dbuf = B == 0 ? st2 : B == 1 ? st0 : st1;
+    barrier();
+    issue_stage(t + 2, dbuf);
+    v16f s[C::KB];
     {
+      constexpr int NS = C::DS * C::KB;
+      auto load = [&](int j) {
+        const int kb = j / C::DS, ds = j % C::DS;
+        return *(const frag*)(rbuf + k_rd[ds % NKR] + (ds / NKR) * 256 + kb * 32 * C::RB);
+      };
+      frag ring[2];
+      ring[0] = load(0);
+#pragma unroll
+      for (int j = 0; j < NS; j++) {
+        if (j + 1 < NS) ring[(j + 1) & 1] = load(j + 1);
+        const int kb = j / C::DS, ds = j % C::DS;
+        if (ds == 0) {
+          const v16f zero = {};
+          s[kb] = M::mma(ring[j & 1], qf[ds], zero);
+        } else {
+          s[kb] = M::mma(ring[j & 1], qf[ds], s[kb]);
+        }
+      }
+    }
+    if (MASKED) {
+      const int key0 = k_lo + t * C::BN;
       const int q = wr0 + nn;
 #pragma unroll
       for (int kb = 0; kb < C::KB; kb++)
@@ -229,162 +246,68 @@ fwd_short_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __re
           for (int jx = 0; jx < 4; jx++) {
             const int key = key0 + kb * 32 + 8 * i + 4 * hh + jx;
             const bool ok = key < k_hi && (!CAUSAL || key <= q + diag);
-            if (!ok) sn[kb][4 * i + jx] = kNegInf;
+            if (!ok) s[kb][4 * i + jx] = kNegInf;
           }
-    }
-  };
-  // row maximum of a new tile: decide whether the reference moves (applied to
-  // O and l once the previous tile's P V is in)
-  float xmax = kNegInf;
-  auto maxdec_b = [&] {
-    const float x = xmax;
-    resc = __any(x > m + kTau);
-    if (resc) {
-      const float mnew = fmaxf(m, x);
-      const float r = mnew == kNegInf ? 0.0f : mnew;
-      alpha = fast_exp2(m - r);            // 0 when m was -inf
-      m = mnew;
-      rf = r;
-    }
-  };
-  // S(t+1)^T = K Q^T with the exponentials of tile t spread over its steps:
-  // each step loads the K fragment LA steps ahead, issues one MFMA and a
-  // fixed share of the vector work; a scheduling barrier keeps that order
-  // (and the register footprint) fixed.
-  constexpr int LA = 3;
-  auto sblock = [&](const char* st, v16f* sd, const v16f* sc) {
-    constexpr bool DS_ = true, DE = true;
-    constexpr int NS = C::DS * C::KB;
-    constexpr int EPS = 16 * C::KB / NS;         // exponentials per step
-    auto load = [&](int j) {
-      const int kb = j / C::DS, ds = j % C::DS;
-      return *(const frag*)(st + k_rd[ds % NKR] + (ds / NKR) * 256 + kb * 32 * C::RB);
-    };
-    frag ring[LA + 1];
-    if (DS_) {
-#pragma unroll
-      for (int j = 0; j < LA; j++) ring[j] = load(j);
-    }
-    float ls = 0.0f;
-    v8f pv;
-#pragma unroll
-    for (int j = 0; j < NS; j++) {
-      if (DS_) {
-        if (j + LA < NS) ring[(j + LA) % (LA + 1)] = load(j + LA);
-        const int kb = j / C::DS, ds = j % C::DS;
-        if (ds == 0) {
-          const v16f zero = {};
-          sd[kb] = M::mma(ring[j % (LA + 1)], qf[ds], zero);
-        } else {
-          sd[kb] = M::mma(ring[j % (LA + 1)], qf[ds], sd[kb]);
-        }
-      }
-      if (DE) {
-#pragma unroll
-        for (int u = 0; u < EPS; u++) {
-          const int idx = j * EPS + u, gi = idx / 8, e = idx % 8;
-          const float p = fast_exp2(__builtin_fmaf(sc[gi / 2][8 * (gi % 2) + e], c, -rf));
-          pv[e] = p;
-          ls += p;
-          if (e == 7) pf[gi / 2][gi % 2] = M::cvt(pv);
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    return ls;
-  };
-  // O^T += V(t)^T P(t)^T with the row maximum of tile t+1 spread over its steps
-  auto pblock = [&](auto do_m, const char* st, const v16f* sn) {
-    constexpr bool DP = true, DM = decltype(do_m)::value;
-    constexpr int NP = C::KB * 2 * C::DB;
-    constexpr int MPS = 16 * C::KB / NP;         // score elements per step
-    const char* vl = st + C::TILE;
-    auto load = [&](int j) {
-      const int kb = j / (2 * C::DB), ks = (j / C::DB) % 2, db = j % C::DB;
-      const int off = (kb * 32 + 16 * ks) * C::RB;
-      const char* va = vl + v_rd[db % NVR] + (db / NVR) * 256 + off;
-      v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)va);
-      v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(va + 8 * C::RB));
-      return __builtin_bit_cast(frag, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-    };
-    frag ring[LA + 1];
-    if (DP) {
-#pragma unroll
-      for (int j = 0; j < LA; j++) ring[j] = load(j);
     }
     float x = kNegInf;
 #pragma unroll
-    for (int j = 0; j < NP; j++) {
-      if (DP) {
-        if (j + LA < NP) ring[(j + LA) % (LA + 1)] = load(j + LA);
-        const int kb = j / (2 * C::DB), ks = (j / C::DB) % 2, db = j % C::DB;
-        o[db] = M::mma(ring[j % (LA + 1)], pf[kb][ks], o[db]);
-      }
-      if (DM) {
+    for (int kb = 0; kb < C::KB; kb++)
 #pragma unroll
-        for (int u = 0; u < MPS; u++) {
-          const int idx = j * MPS + u;
-          x = fmaxf(x, sn[idx / 16][idx % 16]);
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    if (DM) xmax = pair_max(x) * c;
-  };
-  auto barrier = [] {
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-    asm volatile("" ::: "memory");
-  };
-
-  // One step t (-1 <= t < n_tiles) of every wave: stage t+1 (K(t+1), V(t))
-  // is read from buffer (t+1) % 3 while stage t+3 is fetched into buffer t % 3.
-  //   S(t+1)^T = K(t+1) Q^T   with the exponentials of tile t in between;
-  //   O^T += V(t)^T P(t)^T    with the mask and row maximum of tile t+1.
-  // The two waves on a SIMD (one from each resident workgroup) both run this
-  // mix, so matrix instructions of one issue while the other's vector
-  // instructions run.
-  auto step = [&](auto bi, auto masked, int t) {
-    constexpr int B = decltype(bi)::value;
-    constexpr bool MASKED = decltype(masked)::value;
-    char* dbuf = B == 0 ? st0 : B == 1 ? st1 : st2;
-    const char* rbuf = B == 0 ? st1 : B == 1 ? st2 : st0;
-    v16f* scur = sacc[B];
-    v16f* snx = sacc[(B + 1) % 3];
-    barrier();
-    issue_stage(t + 3, dbuf);
-    if (resc) {
+      for (int e = 0; e < 16; e++) x = fmaxf(x, s[kb][e]);
+    x = pair_max(x) * c;
+    if (__any(x > m + kTau)) {
+      const float mnew = fmaxf(m, x);
+      const float r = mnew == kNegInf ? 0.0f : mnew;
+      const float alpha = fast_exp2(m - r);      // 0 when m was -inf
+      m = mnew;
       l *= alpha;
 #pragma unroll
       for (int db = 0; db < C::DB; db++)
 #pragma unroll
         for (int e = 0; e < 16; e++) o[db][e] *= alpha;
     }
-    l += sblock(rbuf, snx, scur);
-    if (MASKED) {
-      mask(snx, t + 1);
-      pblock(IC<0>(), rbuf, snx);
-      float x = kNegInf;
+    const float ref = m == kNegInf ? 0.0f : m;
+    frag pf[C::KB][2];
 #pragma unroll
-      for (int kb = 0; kb < C::KB; kb++)
+    for (int kb = 0; kb < C::KB; kb++)
 #pragma unroll
-        for (int e = 0; e < 16; e++) x = fmaxf(x, snx[kb][e]);
-      xmax = pair_max(x) * c;
-    } else {
-      pblock(IC<1>(), rbuf, snx);
+      for (int ks = 0; ks < 2; ks++) {
+        v8f pv;
+#pragma unroll
+        for (int e = 0; e < 8; e++) {
+          const float p = fast_exp2(__builtin_fmaf(s[kb][8 * ks + e], c, -ref));
+          pv[e] = p;
+          l += p;
+        }
+        pf[kb][ks] = M::cvt(pv);
+      }
+    {
+      constexpr int NP = C::KB * 2 * C::DB;
+      const char* vl = rbuf + C::TILE;
+      auto load = [&](int j) {
+        const int kb = j / (2 * C::DB), ks = (j / C::DB) % 2, db = j % C::DB;
+        const int off = (kb * 32 + 16 * ks) * C::RB;
+        const char* va = vl + v_rd[db % NVR] + (db / NVR) * 256 + off;
+        v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)va);
+        v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(va + 8 * C::RB));
+        return __builtin_bit_cast(frag, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      };
+      frag ring[2];
+      ring[0] = load(0);
+#pragma unroll
+      for (int j = 0; j < NP; j++) {
+        if (j + 1 < NP) ring[(j + 1) & 1] = load(j + 1);
+        const int kb = j / (2 * C::DB), ks = (j / C::DB) % 2, db = j % C::DB;
+        o[db] = M::mma(ring[j & 1], pf[kb][ks], o[db]);
+      }
     }
-    maxdec_b();
-    __builtin_amdgcn_s_waitcnt(0x0070 | 0x0F00 | (2 * C::NI));   // stage t+2 complete
+    __builtin_amdgcn_s_waitcnt(0x0070 | 0x0F00 | (2 * C::NI));   // stage t+1 complete
   };
 
-  // Steps run from t = -1 to the wave's last tile with any allowed key
-  // (causal: a prefix of the tiles); scores of tiles past the key range are
-  // masked to -inf, and before the first tile the "current" scores are -inf,
-  // so their probabilities are exactly 0 and every step is the same code.
-  // After its last tile a wave only keeps the barriers and its share of the
-  // loads going until the workgroup's last tile.
+  // Steps run over the wave's tiles with an allowed key (causal: a prefix);
+  // tiles that need no mask for any row of the wave come first, the masked
+  // ones (key-range tail, causal diagonal) are a suffix. After its last tile
+  // a wave only keeps the barriers and its share of the loads going.
   if (n_tiles > 0) {
     int t_last = n_tiles - 1;
     if (CAUSAL) {
@@ -393,10 +316,7 @@ fwd_short_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __re
     }
     issue_stage(0, st0);
     issue_stage(1, st1);
-    __builtin_amdgcn_s_waitcnt(0x0070 | 0x0F00);
-    __syncthreads();
-    // tiles whose scores need no mask for any row of this wave come first;
-    // the masked ones (key-range tail, causal diagonal) are a suffix
+    __builtin_amdgcn_s_waitcnt(0x0070 | 0x0F00 | (2 * C::NI));   // stage 0 complete
     int u_mask = (k_hi - k_lo) / C::BN;
     if (CAUSAL) {
       const int lim2 = wr0 + diag - k_lo + 1;
@@ -404,34 +324,27 @@ fwd_short_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __re
     }
     const IC<0> P;
     const IC<1> Mk;
-    int t = -1;
-    const int t_plain = min(t_last, u_mask - 2);      // last step whose new tile is unmasked
-    for (; t + 2 <= t_plain; t += 3) {
-      step(IC<2>(), P, t);
-      step(IC<0>(), P, t + 1);
-      step(IC<1>(), P, t + 2);
+    int t = 0;
+    const int t_plain = min(t_last + 1, u_mask);
+    for (; t + 2 < t_plain; t += 3) {
+      step(IC<0>(), P, t);
+      step(IC<1>(), P, t + 1);
+      step(IC<2>(), P, t + 2);
     }
     for (; t + 2 <= t_last; t += 3) {
-      step(IC<2>(), Mk, t);
-      step(IC<0>(), Mk, t + 1);
-      step(IC<1>(), Mk, t + 2);
+      step(IC<0>(), Mk, t);
+      step(IC<1>(), Mk, t + 1);
+      step(IC<2>(), Mk, t + 2);
     }
-    if (t <= t_last) { step(IC<2>(), Mk, t); t++; }
     if (t <= t_last) { step(IC<0>(), Mk, t); t++; }
+    if (t <= t_last) { step(IC<1>(), Mk, t); t++; }
     for (; t < n_tiles; t++) {
-      const int bsel = (t + 3) % 3;
+      const int bsel = (t + 2) % 3;
       barrier();
-      issue_stage(t + 3, bsel == 0 ? st0 : bsel == 1 ? st1 : st2);
+      issue_stage(t + 2, bsel == 0 ? st0 : bsel == 1 ? st1 : st2);
       __builtin_amdgcn_s_waitcnt(0x0070 | 0x0F00 | (2 * C::NI));
     }
     __builtin_amdgcn_s_waitcnt(0x0070 | 0x0F00);
-    if (resc) {                    // a reference change not yet applied (cannot happen: the
-      l *= alpha;                  // last scores a wave looks at are fully masked)
-#pragma unroll
-      for (int db = 0; db < C::DB; db++)
-#pragma unroll
-        for (int e = 0; e < 16; e++) o[db][e] *= alpha;
-    }
   }
 
   // ---- epilogue: normalise, logsumexp, store

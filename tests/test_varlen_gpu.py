@@ -67,9 +67,12 @@ def test_varlen_against_oracle(gpu_lib, case, dtype, D):
     check(o, lse, q, k, v, cu_q, cu_k, causal, scale, f"case {case}")
 
 
-@pytest.mark.parametrize("S,causal", [(1000, False), (2500, True)])
+@pytest.mark.parametrize("S,causal", [(2000, False), (2500, True)])
 def test_varlen_equal_lengths_bitwise_equal_dense(gpu_lib, S, causal):
-    """B sequences of one length: the packed path gives the dense path's bits, transposed in layout."""
+    """B sequences of one length: the packed path gives the dense path's bits, transposed in layout.
+
+    (Lengths where the dense entry point also runs the main kernel: shorter ranges go to the
+    short-range kernel, whose different tiling changes the rounding order.)"""
     note(f"varlen vs dense S{S} causal={causal}")
     B, H, D = 2, 4, 128
     q, k, v = inputs.qkv(B, H, S, S, D, seed=5, dtype=torch.bfloat16, device="cuda")
