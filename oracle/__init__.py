@@ -42,3 +42,4 @@ from .fp8 import (  # noqa: F401
     dequantize_blocks,
 )
 from .fp8_pipeline import fp8_attention_sim, rmse  # noqa: F401
+from .rope import rope_angles, rotary, rotary_f32, rope_hadamard_quantize  # noqa: F401

@@ -508,3 +508,62 @@ def test_varlen_rejects_bad_offsets():
         oracle.attention_varlen(q, k, v, np.array([0, 5, 4]), cu_k, False, 1.0)
     with pytest.raises(ValueError):
         oracle.attention_varlen(q, k, v, cu_q, np.array([1, 3, 7]), False, 1.0)
+
+
+# ---------------------------------------------------------------- rotary embedding ahead of the quantizer
+
+def test_rotary_worked_example():
+    """D = 4, quarter turn on pair 0 and half turn on pair 1, by hand."""
+    x = np.array([[1.0, 2.0, 3.0, 4.0]])
+    cos = np.array([[0.0, -1.0]])
+    sin = np.array([[1.0, 0.0]])
+    # interleaved pairs (0,1), (2,3): (1,2) -> (-2, 1); (3,4) -> (-3, -4)
+    assert np.array_equal(oracle.rotary(x, cos, sin, 0), [[-2.0, 1.0, -3.0, -4.0]])
+    # halves (0,2), (1,3): (1,3) -> (-3, 1); (2,4) -> (-2, -4)
+    assert np.array_equal(oracle.rotary(x, cos, sin, 1), [[-3.0, -2.0, 1.0, -4.0]])
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+def test_rotary_is_a_rotation_with_relative_positions(mode):
+    """Pair norms are kept, and the dot product of two rotated rows depends only on their distance."""
+    S, D = 40, 16
+    th = oracle.rope_angles(S, D)
+    c, s = np.cos(th), np.sin(th)
+    q, k = _rand((S, D), 1), _rand((S, D), 2)
+    rq, rk = oracle.rotary(q, c, s, mode), oracle.rotary(k, c, s, mode)
+    a = np.arange(D // 2) * 2 if mode == 0 else np.arange(D // 2)
+    b = a + 1 if mode == 0 else a + D // 2
+    assert np.abs(rq[:, a] ** 2 + rq[:, b] ** 2 - q[:, a] ** 2 - q[:, b] ** 2).max() < TIGHT
+    # the same two vectors placed at positions (m, n) and (m + t, n + t)
+    qq = np.tile(q[3], (S, 1))
+    kk = np.tile(k[5], (S, 1))
+    rqq, rkk = oracle.rotary(qq, c, s, mode), oracle.rotary(kk, c, s, mode)
+    dots = [rqq[m] @ rkk[m - 7] for m in range(7, S)]
+    assert np.ptp(dots) < 1e-10
+    assert abs(rqq[0] @ rkk[0] - q[3] @ k[5]) < TIGHT           # position 0 is the identity
+
+
+def test_rotary_halves_equal_interleaved_after_permutation():
+    S, D = 9, 8
+    th = oracle.rope_angles(S, D)
+    x = _rand((S, D), 3)
+    perm = np.concatenate([np.arange(0, D, 2), np.arange(1, D, 2)])   # interleaved -> halves order
+    inter = oracle.rotary(x, np.cos(th), np.sin(th), 0)
+    halves = oracle.rotary(x[:, perm], np.cos(th), np.sin(th), 1)
+    assert np.array_equal(halves, inter[:, perm])
+
+
+def test_rotary_float32_within_rounding_and_fused_quantizer():
+    """The float32 mirror stays within a few float32 ulps; with zero angles the fused quantizer is the plain one."""
+    S, D = 64, 128
+    th = oracle.rope_angles(S, D)
+    c32, s32 = np.cos(th).astype(np.float32), np.sin(th).astype(np.float32)
+    x = _rand((2, 1, S, D), 4).astype(np.float32)
+    exact = oracle.rotary(x, c32, s32, 1)
+    mirror = oracle.rotary_f32(x, c32, s32, 1)
+    assert np.all(np.abs(mirror - exact) <= 4 * np.finfo(np.float32).eps * (np.abs(x).max() + 1))
+    signs = inputs.signs(D, 0).numpy()
+    ones, zeros = np.ones((S, D // 2), np.float32), np.zeros((S, D // 2), np.float32)
+    c1, s1 = oracle.rope_hadamard_quantize(x, ones, zeros, 0, signs)
+    c2, s2 = oracle.hadamard_quantize(x, signs)
+    assert np.array_equal(c1, c2) and np.array_equal(s1, s2)
