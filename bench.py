@@ -143,6 +143,10 @@ def fp8_point(steps=10, warmup=3):
     vq_ms, _ = time_launches(lambda: attn.quant_per_tensor(v, out=(v8, vs)), steps, warmup)
     att_ms, _ = time_launches(lambda: attn.fwd_fp8(q8, k8, v8, qs, ks, vs, False, scale, out=o, lse=lse),
                               steps, warmup)
+    # rotary embedding fused ahead of the transform (tables for 8K positions, half pairs)
+    cos, sin = inputs.rope_tables(S, D, device="cuda")
+    rope_ms, _ = time_launches(lambda: attn.rope_hadamard_quant(q, sg, cos, sin, mode=1, out=(q8, qs)),
+                               steps, warmup)
     fl = flops(B, H, S, S, D, False)
     pre_bytes = B * H * S * D * (2 + 1) + B * H * (S // 64) * 4
     vq_bytes = B * H * S * D * (2 + 2 + 1)
@@ -150,6 +154,8 @@ def fp8_point(steps=10, warmup=3):
     res = {"B": B, "H": H, "S": S, "D": D, "attn_ms": round(att_ms, 4),
            "attn_tflops": round(fl / att_ms / 1e9, 1), "attn_pct_fp8_peak": round(100 * fl / att_ms / 1e9 / PEAK_FP8, 1),
            "hadamard_quant_ms": round(pre_ms, 4), "hadamard_quant_gbps": round(pre_bytes / pre_ms / 1e6, 1),
+           "rope_hadamard_quant_ms": round(rope_ms, 4),
+           "rope_hadamard_quant_gbps": round(pre_bytes / rope_ms / 1e6, 1),
            "v_quant_ms": round(vq_ms, 4), "v_quant_gbps": round(vq_bytes / vq_ms / 1e6, 1),
            "pipeline_ms": round(e2e, 4), "pipeline_tflops": round(fl / e2e / 1e9, 1)}
     del q, k, v, q8, k8, v8, o, lse

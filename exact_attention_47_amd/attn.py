@@ -43,6 +43,7 @@ _SIGS = {
     "quant_per_tensor": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp]),
     "attn_fwd_fp8": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i, _i, _vp]),
     "attn_fwd_varlen": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _f, _i, _vp]),
+    "rope_hadamard_quant": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp]),
 }
 
 
@@ -223,6 +224,34 @@ def hadamard_quant(x, signs, block_rows=64, apply_hadamard=True, out=None):
     _check("hadamard_quant", load().hadamard_quant(_ptr(x), _ptr(x8), _ptr(scales), _ptr(signs), B, H, S,
                                                    D, block_rows, int(bool(apply_hadamard)),
                                                    _DTYPE[x.dtype], st))
+    return x8, scales
+
+
+def rope_hadamard_quant(x, signs, cos, sin, mode=0, block_rows=64, out=None):
+    """Rotary embedding (tables cos/sin float32 [S, D/2] on the GPU; mode 0 interleaved pairs,
+    1 half pairs) followed by hadamard_quant, in one pass: (codes uint8 [B,H,S,D], scales)."""
+    _need_gpu(x, signs, cos, sin)
+    if x.dim() != 4 or x.dtype not in (torch.float16, torch.bfloat16):
+        raise ValueError("x must be a float16/bfloat16 [B, H, S, D] tensor")
+    B, H, S, D = x.shape
+    if signs.dtype != torch.int8 or signs.shape != (D,):
+        raise ValueError("signs must be int8 [D]")
+    if cos.dtype != torch.float32 or sin.dtype != torch.float32 or tuple(cos.shape) != (S, D // 2) \
+            or tuple(sin.shape) != (S, D // 2):
+        raise ValueError("cos and sin must be float32 [S, D/2]")
+    nb = (S + block_rows - 1) // block_rows
+    if out is None:
+        x8 = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+        scales = torch.empty((B, H, nb), dtype=torch.float32, device=x.device)
+    else:
+        x8, scales = out
+        if (x8.shape != x.shape or x8.dtype != torch.uint8 or scales.shape != (B, H, nb)
+                or scales.dtype != torch.float32):
+            raise ValueError("out must be (uint8 like x, float32 [B, H, nblk])")
+        _need_gpu(x8, scales)
+    _check("rope_hadamard_quant", load().rope_hadamard_quant(
+        _ptr(x), _ptr(x8), _ptr(scales), _ptr(signs), _ptr(cos), _ptr(sin), B, H, S, D, block_rows, int(mode),
+        _DTYPE[x.dtype], _stream(x.device)))
     return x8, scales
 
 

@@ -252,6 +252,22 @@ int hadamard_quant(const void* x, void* x8, float* scales, const signed char* si
   return e == hipSuccess ? ATTN_OK : (e == hipErrorNotSupported ? ATTN_ERR_UNSUPPORTED : ATTN_ERR_LAUNCH);
 }
 
+int rope_hadamard_quant(const void* x, void* x8, float* scales, const signed char* signs, const float* cos_t,
+                        const float* sin_t, int B, int H, int S, int D, int block_rows, int rope_mode,
+                        int in_dtype, void* stream) {
+  if (!x || !x8 || !scales || !signs || !cos_t || !sin_t) return ATTN_ERR_INVALID_ARG;
+  if (B <= 0 || H <= 0 || S <= 0 || D <= 0 || block_rows <= 0) return ATTN_ERR_INVALID_ARG;
+  if (rope_mode != 0 && rope_mode != 1) return ATTN_ERR_INVALID_ARG;
+  if (in_dtype != ATTN_BF16 && in_dtype != ATTN_F16) return ATTN_ERR_INVALID_ARG;
+  if ((D != 64 && D != 128 && D != 256) || block_rows != 64) return ATTN_ERR_UNSUPPORTED;
+  if (!aligned(x, 16) || !aligned(x8, 16) || !aligned(scales, 4) || !aligned(signs, 8) || !aligned(cos_t, 16) ||
+      !aligned(sin_t, 16))
+    return ATTN_ERR_MISALIGNED;
+  const hipError_t e = attn::launch_rope_hadamard_quant(x, x8, scales, signs, cos_t, sin_t, B, H, S, D, rope_mode,
+                                                        in_dtype, (hipStream_t)stream);
+  return e == hipSuccess ? ATTN_OK : (e == hipErrorNotSupported ? ATTN_ERR_UNSUPPORTED : ATTN_ERR_LAUNCH);
+}
+
 int quant_per_tensor(const void* x, void* x8, float* scale, int B, int H, int S, int D, int in_dtype,
                      int write_transposed, void* stream) {
   if (!x || !x8 || !scale) return ATTN_ERR_INVALID_ARG;

@@ -22,6 +22,14 @@
 // taken in the order 1, 2, ..., D/2. Other block sizes use a general kernel
 // that spreads a row over D/8 lanes and re-reads the block for its second pass.
 //
+// rope_hadamard_quant: the same with rotary position embedding applied to
+// each row first, in the registers that already hold it ([GN] "Niedrige
+// FP8-Praezision und incoherent processing": the transform is memory-bound
+// and costs nothing extra when fused with a preceding memory-bound operation
+// such as rotary embedding). The angles come as cos/sin tables [S][D/2]
+// float32 shared by every (b, h), so they stay in cache; both coordinates of
+// a pair (interleaved 2j, 2j+1, or halves j, j + D/2) are in the same lane.
+//
 // quant_per_tensor: one scale for the whole tensor. Launch 1 clears the
 // running maximum, launch 2 reduces max |x| per workgroup and folds it in with
 // an integer atomic max on the float bits (exact for non-negative floats and
@@ -158,11 +166,23 @@ hadamard_quant_kernel(const T* __restrict__ X, uint8_t* __restrict__ X8, float* 
   }
 }
 
-// one 64-row block per workgroup, four lanes per row (see the header)
-template <typename T, int D>
+// x' = x * c - y * s, y' = y * c + x * s with every product and sum rounded
+// on its own (no fused multiply-add: the result feeds the quantizer, whose
+// codes must not depend on how the compiler contracts)
+__device__ __forceinline__ void rotate(float& x, float& y, float c, float s) {
+#pragma clang fp contract(off)
+  const float xc = x * c, ys = y * s, yc = y * c, xs = x * s;
+  x = xc - ys;
+  y = yc + xs;
+}
+
+// one 64-row block per workgroup, four lanes per row (see the header);
+// ROPE: 0 none, 1 rotary embedding on interleaved pairs, 2 on half pairs
+template <typename T, int D, int ROPE>
 __global__ void __launch_bounds__(256)
 hadamard_quant64_kernel(const T* __restrict__ X, uint8_t* __restrict__ X8, float* __restrict__ scales,
-                        const signed char* __restrict__ signs, int S, int n_blk, int apply, float rsqrt_d)
+                        const signed char* __restrict__ signs, int S, int n_blk, int apply, float rsqrt_d,
+                        const float* __restrict__ cos_t, const float* __restrict__ sin_t)
 {
   constexpr int NK = D / 32;                 // 8-element chunks per lane
   __shared__ float red[4];
@@ -183,6 +203,33 @@ hadamard_quant64_kernel(const T* __restrict__ X, uint8_t* __restrict__ X8, float
     for (int k = 0; k < NK; k++)
 #pragma unroll
       for (int i = 0; i < 8; i++) u[k][i] = 0.0f;
+  }
+  // rotary embedding of position r (tables [S][D/2] float32) before the
+  // transform: both coordinates of every pair sit in this lane
+  if (ROPE != 0 && valid) {
+    const float* cr = cos_t + (size_t)r * (D / 2);
+    const float* sr = sin_t + (size_t)r * (D / 2);
+    if (ROPE == 1) {                           // pairs (2j, 2j+1): j = 16k + 4*sub + i/2
+#pragma unroll
+      for (int k = 0; k < NK; k++) {
+        const float4 c4 = *(const float4*)(cr + 16 * k + 4 * sub);
+        const float4 s4 = *(const float4*)(sr + 16 * k + 4 * sub);
+        rotate(u[k][0], u[k][1], c4.x, s4.x);
+        rotate(u[k][2], u[k][3], c4.y, s4.y);
+        rotate(u[k][4], u[k][5], c4.z, s4.z);
+        rotate(u[k][6], u[k][7], c4.w, s4.w);
+      }
+    } else {                                   // pairs (j, j + D/2): chunks k and k + NK/2
+#pragma unroll
+      for (int k = 0; k < NK / 2; k++) {
+        const float4 c0 = *(const float4*)(cr + 32 * k + 8 * sub), c1 = *(const float4*)(cr + 32 * k + 8 * sub + 4);
+        const float4 s0 = *(const float4*)(sr + 32 * k + 8 * sub), s1 = *(const float4*)(sr + 32 * k + 8 * sub + 4);
+        const float cc[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+        const float ss[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+#pragma unroll
+        for (int i = 0; i < 8; i++) rotate(u[k][i], u[k + NK / 2][i], cc[i], ss[i]);
+      }
+    }
   }
   if (apply) {
 #pragma unroll
@@ -379,30 +426,36 @@ __global__ void finish_scale_kernel(float* scale_and_bits) {
   *scale_and_bits = a > 0.0f ? __fdiv_rn(a, kE4M3Max) : 1.0f;
 }
 
+template <typename T, int ROPE>
+hipError_t hq64(const void* x, void* x8, float* scales, const signed char* signs, const float* cos_t,
+                const float* sin_t, int B, int H, int S, int D, int apply, hipStream_t st) {
+  const int n_blk = (S + 63) / 64;
+  const dim3 grid((unsigned)(B * H * n_blk));
+  const float r = (float)(1.0 / __builtin_sqrt((double)D));
+  switch (D) {
+    case 64:
+      hipLaunchKernelGGL((hadamard_quant64_kernel<T, 64, ROPE>), grid, dim3(256), 0, st, (const T*)x,
+                         (uint8_t*)x8, scales, signs, S, n_blk, apply, r, cos_t, sin_t);
+      return hipGetLastError();
+    case 128:
+      hipLaunchKernelGGL((hadamard_quant64_kernel<T, 128, ROPE>), grid, dim3(256), 0, st, (const T*)x,
+                         (uint8_t*)x8, scales, signs, S, n_blk, apply, r, cos_t, sin_t);
+      return hipGetLastError();
+    case 256:
+      hipLaunchKernelGGL((hadamard_quant64_kernel<T, 256, ROPE>), grid, dim3(256), 0, st, (const T*)x,
+                         (uint8_t*)x8, scales, signs, S, n_blk, apply, r, cos_t, sin_t);
+      return hipGetLastError();
+  }
+  return hipErrorNotSupported;
+}
+
 template <typename T>
 hipError_t hq_t(const void* x, void* x8, float* scales, const signed char* signs, int B, int H, int S,
                 int D, int block_rows, int apply, hipStream_t st) {
   const int n_blk = (S + block_rows - 1) / block_rows;
   const dim3 grid((unsigned)(B * H * n_blk));
   const float r = (float)(1.0 / __builtin_sqrt((double)D));
-  if (block_rows == 64) {
-    switch (D) {
-      case 64:
-        hipLaunchKernelGGL((hadamard_quant64_kernel<T, 64>), grid, dim3(256), 0, st, (const T*)x,
-                           (uint8_t*)x8, scales, signs, S, n_blk, apply, r);
-        return hipGetLastError();
-      case 128:
-        hipLaunchKernelGGL((hadamard_quant64_kernel<T, 128>), grid, dim3(256), 0, st, (const T*)x,
-                           (uint8_t*)x8, scales, signs, S, n_blk, apply, r);
-        return hipGetLastError();
-      case 256:
-        hipLaunchKernelGGL((hadamard_quant64_kernel<T, 256>), grid, dim3(256), 0, st, (const T*)x,
-                           (uint8_t*)x8, scales, signs, S, n_blk, apply, r);
-        return hipGetLastError();
-      default:
-        return hipErrorNotSupported;
-    }
-  }
+  if (block_rows == 64) return hq64<T, 0>(x, x8, scales, signs, nullptr, nullptr, B, H, S, D, apply, st);
   switch (D) {
     case 64:
       hipLaunchKernelGGL((hadamard_quant_kernel<T, 64>), grid, dim3(256), 0, st, (const T*)x, (uint8_t*)x8,
@@ -449,6 +502,16 @@ hipError_t launch_hadamard_quant(const void* x, void* x8, float* scales, const s
                                  hipStream_t st) {
   if (in_dtype == 2) return hq_t<__bf16>(x, x8, scales, signs, B, H, S, D, block_rows, apply_hadamard, st);
   return hq_t<_Float16>(x, x8, scales, signs, B, H, S, D, block_rows, apply_hadamard, st);
+}
+
+hipError_t launch_rope_hadamard_quant(const void* x, void* x8, float* scales, const signed char* signs,
+                                      const float* cos_t, const float* sin_t, int B, int H, int S, int D,
+                                      int rope_mode, int in_dtype, hipStream_t st) {
+  if (in_dtype == 2)
+    return rope_mode == 0 ? hq64<__bf16, 1>(x, x8, scales, signs, cos_t, sin_t, B, H, S, D, 1, st)
+                          : hq64<__bf16, 2>(x, x8, scales, signs, cos_t, sin_t, B, H, S, D, 1, st);
+  return rope_mode == 0 ? hq64<_Float16, 1>(x, x8, scales, signs, cos_t, sin_t, B, H, S, D, 1, st)
+                        : hq64<_Float16, 2>(x, x8, scales, signs, cos_t, sin_t, B, H, S, D, 1, st);
 }
 
 hipError_t launch_quant_per_tensor(const void* x, void* x8, float* scale, int B, int H, int S, int D,

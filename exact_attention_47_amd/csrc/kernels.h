@@ -61,6 +61,9 @@ hipError_t launch_combine(const FwdArgs& a, hipStream_t st);
 hipError_t launch_hadamard_quant(const void* x, void* x8, float* scales, const signed char* signs,
                                  int B, int H, int S, int D, int block_rows, int apply_hadamard,
                                  int in_dtype, hipStream_t st);
+hipError_t launch_rope_hadamard_quant(const void* x, void* x8, float* scales, const signed char* signs,
+                                      const float* cos_t, const float* sin_t, int B, int H, int S, int D,
+                                      int rope_mode, int in_dtype, hipStream_t st);
 hipError_t launch_quant_per_tensor(const void* x, void* x8, float* scale, int B, int H, int S, int D,
                                    int in_dtype, int write_transposed, hipStream_t st);
 hipError_t launch_fwd_fp8(const void* q8, const void* k8, const void* v8, const float* qs,

@@ -119,3 +119,15 @@ def sequence_lengths(n_seq: int, total: int, seed: int, min_len: int = 1):
     cuts = torch.randperm(total - n_seq * min_len + n_seq - 1, generator=g)[:n_seq - 1].sort().values
     edges = [-1] + cuts.tolist() + [total - n_seq * min_len + n_seq - 1]
     return [edges[i + 1] - edges[i] - 1 + min_len for i in range(n_seq)]
+
+
+def rope_tables(s: int, d: int, base: float = 10000.0, device="cpu"):
+    """cos and sin tables float32 [S, D/2] of the standard rotary angles p * base^(-2j/D).
+
+    Workload inputs for the fused rotary + Hadamard quantizer (a model supplies
+    such tables); formed in float64 and rounded once to float32.
+    """
+    j = np.arange(d // 2, dtype=np.float64)
+    th = np.arange(s, dtype=np.float64)[:, None] * base ** (-2.0 * j / d)[None, :]
+    return (torch.from_numpy(np.cos(th).astype(np.float32)).to(device),
+            torch.from_numpy(np.sin(th).astype(np.float32)).to(device))

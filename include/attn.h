@@ -183,6 +183,31 @@ int hadamard_quant(const void* x, void* x8, float* scales, const signed char* si
                    int in_dtype, void* stream);
 
 /*
+ * rope_hadamard_quant -- hadamard_quant with rotary position embedding applied
+ * to every row first, fused into the same pass over x ([GN] "Niedrige
+ * FP8-Praezision und incoherent processing": the Hadamard transform is bound
+ * by memory bandwidth and costs nothing extra when fused with a preceding
+ * memory-bound operation such as rotary embedding).
+ *
+ *   x, x8, scales, signs, B, H, S, D, in_dtype  as for hadamard_quant
+ *   cos_t, sin_t  device float32 tables [S][D/2] (16-byte aligned): row p, pair
+ *                 j holds cos / sin of that position's angle for pair j; shared
+ *                 by every (b, h)
+ *   rope_mode     0: pairs (2j, 2j+1); 1: pairs (j, j + D/2)
+ *   block_rows    must be 64
+ *
+ * Row p of each (b, h) becomes x'_a = x_a cos - x_b sin, x'_b = x_b cos + x_a
+ * sin for each pair (a, b), every product and sum rounded to float32 on its
+ * own (no fused multiply-add), and then goes through hadamard_quant's
+ * transform and block quantization unchanged (codes are reproducible bit for
+ * bit). Returns ATTN_ERR_UNSUPPORTED for block_rows != 64 or D not in
+ * {64, 128, 256}; other errors as for hadamard_quant.
+ */
+int rope_hadamard_quant(const void* x, void* x8, float* scales, const signed char* signs,
+                        const float* cos_t, const float* sin_t, int B, int H, int S, int D,
+                        int block_rows, int rope_mode, int in_dtype, void* stream);
+
+/*
  * quant_per_tensor -- E4M3 quantization with one scale for the whole tensor
  * (four small launches on `stream`: clear, max |x|, quantize, final scale).
  * Used for V on the FP8 path and for the plain per-tensor FP8 baseline

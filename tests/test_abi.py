@@ -135,3 +135,24 @@ def test_varlen_validation_rejects(kw, code):
 def test_varlen_empty_query_batch_is_a_no_op():
     # zero query rows: nothing to compute, NULL q/o/lse allowed, nothing enqueued
     assert varlen(q=None, o=None, lse=None, total_q=0, max_q=0) == attn.OK
+
+
+def rope(**kw):
+    a = dict(x=P, x8=P, sc=P, sg=P, c=P, s=P, B=1, H=2, S=128, D=128, br=64, mode=0, dt=2)
+    a.update(kw)
+    return attn.load().rope_hadamard_quant(a["x"], a["x8"], a["sc"], a["sg"], a["c"], a["s"], a["B"], a["H"],
+                                           a["S"], a["D"], a["br"], a["mode"], a["dt"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(c=None), attn.ERR_INVALID_ARG),
+    (dict(S=0), attn.ERR_INVALID_ARG),
+    (dict(mode=2), attn.ERR_INVALID_ARG),
+    (dict(dt=0), attn.ERR_INVALID_ARG),
+    (dict(br=32), attn.ERR_UNSUPPORTED),
+    (dict(D=96), attn.ERR_UNSUPPORTED),
+    (dict(s=P + 4), attn.ERR_MISALIGNED),
+])
+def test_rope_hadamard_quant_validation_rejects(kw, code):
+    """Host-side checks of rope_hadamard_quant: each bad argument is refused before anything is enqueued."""
+    assert rope(**kw) == code

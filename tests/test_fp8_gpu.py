@@ -168,3 +168,44 @@ def test_fp8_error_ratio_fullsize(gpu_lib):
     e_p = float(np.sqrt(np.mean(np.concatenate(d_p) ** 2)))
     print(f"    RMSE hadamard+block {e_h:.4e}, plain per-tensor {e_p:.4e}, reduction {e_p / e_h:.2f}x")
     assert e_h <= 0.5 * e_p
+
+
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("mode", [0, 1])
+def test_rope_hadamard_quant_bitexact(gpu_lib, dt, D, mode):
+    """Rotary embedding fused ahead of the Hadamard quantizer: codes and scales bit for bit."""
+    note(f"rope_hadamard_quant {dt} D{D} mode={mode}")
+    B, H, S = 1, 2, 200
+    x = inputs.with_outliers((B, H, S, D), 12, inputs.TENSOR_Q, dtype=dt)
+    x[0, 1, 64:128] = 0                     # an all-zero block
+    sg = inputs.signs(D, 12)
+    cos, sin = inputs.rope_tables(S, D)
+    x8, sc = gpu_lib.rope_hadamard_quant(x.cuda(), sg.cuda(), cos.cuda(), sin.cuda(), mode=mode)
+    torch.cuda.synchronize()
+    rc, rs = oracle.rope_hadamard_quantize(x.float().numpy(), cos.numpy(), sin.numpy(), mode, sg.numpy(), 64)
+    np.testing.assert_array_equal(sc.cpu().numpy().view(np.uint32), rs.astype(np.float32).view(np.uint32))
+    mism = int((x8.cpu().numpy() != rc).sum())
+    assert mism == 0, f"{mism} codes differ"
+
+
+def test_rope_hadamard_quant_fullsize_bitexact_and_zero_angles(gpu_lib):
+    """The FP8 workload's Q tensor (B=2, H=16, S=8192, D=128) with rotary tables of 8K positions;
+    with all angles zero the fused kernel gives the plain quantizer's bytes."""
+    note("rope_hadamard_quant full size B2 H16 S8192 D128")
+    B, H, S, D = 2, 16, 8192, 128
+    x = inputs.with_outliers((B, H, S, D), 0, inputs.TENSOR_Q, dtype=torch.bfloat16)
+    sg = inputs.signs(D, 0)
+    cos, sin = inputs.rope_tables(S, D)
+    xg, sgg = x.cuda(), sg.cuda()
+    x8, sc = gpu_lib.rope_hadamard_quant(xg, sgg, cos.cuda(), sin.cuda(), mode=1)
+    torch.cuda.synchronize()
+    rc, rs = oracle.rope_hadamard_quantize(x.float().numpy(), cos.numpy(), sin.numpy(), 1, sg.numpy(), 64)
+    np.testing.assert_array_equal(sc.cpu().numpy().view(np.uint32), rs.astype(np.float32).view(np.uint32))
+    assert int((x8.cpu().numpy() != rc).sum()) == 0
+    one = torch.ones((S, D // 2), dtype=torch.float32, device="cuda")
+    zero = torch.zeros((S, D // 2), dtype=torch.float32, device="cuda")
+    a8, asc = gpu_lib.rope_hadamard_quant(xg, sgg, one, zero, mode=0)
+    b8, bsc = gpu_lib.hadamard_quant(xg, sgg)
+    torch.cuda.synchronize()
+    assert torch.equal(a8, b8) and torch.equal(asc, bsc)
