@@ -31,6 +31,7 @@ from .attention import (  # noqa: F401
     allowed_mask,
 )
 from .varlen import attention_varlen  # noqa: F401
+from .backward import attention_backward  # noqa: F401
 from .hadamard import sylvester, fwht, random_sign_hadamard  # noqa: F401
 from .fp8 import (  # noqa: F401
     E4M3_MAX,

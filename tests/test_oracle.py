@@ -567,3 +567,50 @@ def test_rotary_float32_within_rounding_and_fused_quantizer():
     c1, s1 = oracle.rope_hadamard_quantize(x, ones, zeros, 0, signs)
     c2, s2 = oracle.hadamard_quantize(x, signs)
     assert np.array_equal(c1, c2) and np.array_equal(s1, s2)
+
+
+# ---------------------------------------------------------------- backward pass
+
+@pytest.mark.parametrize("causal,s_q,s_k", [(False, 13, 21), (True, 17, 17), (True, 9, 30)])
+def test_backward_equals_torch_autograd(causal, s_q, s_k):
+    """The oracle's gradients equal torch autograd through SDPA in float64 (an independent library)."""
+    B, H, D = 2, 2, 16
+    q, k, v = (torch.from_numpy(_rand((B, H, s, D), i)).requires_grad_() for i, s in
+               ((1, s_q), (2, s_k), (3, s_k)))
+    do = _rand((B, H, s_q, D), 4)
+    scale = 0.31
+    mask = torch.from_numpy(oracle.allowed_mask(s_q, s_k, causal))
+    o = torch.nn.functional.scaled_dot_product_attention(q, k, v, attn_mask=mask, scale=scale)
+    o.backward(torch.from_numpy(do))
+    dq, dk, dv = oracle.attention_backward(q.detach().numpy(), k.detach().numpy(), v.detach().numpy(), do,
+                                           causal, scale)
+    for mine, ref in ((dq, q.grad), (dk, k.grad), (dv, v.grad)):
+        assert np.abs(mine - ref.numpy()).max() < 1e-12
+
+
+def test_backward_finite_differences_and_invariants():
+    """Central differences of <dO, O> on a tiny case; the gradient of a shift of all scores of a row is zero."""
+    B, H, S, D = 1, 1, 5, 4
+    q, k, v, do = (_rand((B, H, S, D), i) for i in (5, 6, 7, 8))
+    scale = 0.7
+    dq, dk, dv = oracle.attention_backward(q, k, v, do, True, scale)
+
+    def f(qq, kk, vv):
+        o, _ = oracle.attention(qq, kk, vv, True, scale)
+        return float((o * do).sum())
+
+    eps = 1e-6
+    for x, g, which in ((q, dq, 0), (k, dk, 1), (v, dv, 2)):
+        for idx in [(0, 0, 0, 0), (0, 0, 3, 2), (0, 0, 4, 3)]:
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += eps
+            xm[idx] -= eps
+            args_p = [q, k, v]
+            args_m = [q, k, v]
+            args_p[which], args_m[which] = xp, xm
+            num = (f(*args_p) - f(*args_m)) / (2 * eps)
+            assert abs(num - g[idx]) < 1e-7
+    # adding the same vector c to every key shifts each row's scores by q_i.c: softmax unchanged, so
+    # the directional derivative of <dO, O> along that change, sum_j dK_j . c, is zero
+    c = _rand((D,), 9)
+    assert abs((dk[0, 0].sum(axis=0) * c).sum()) < 1e-12
