@@ -126,6 +126,23 @@ def varlen_point(causal=True, steps=10, warmup=3):
     return res
 
 
+def bwd_point(causal, B=2, H=16, S=8192, D=128, steps=10, warmup=3):
+    """Backward pass (dQ, dK, dV) at the headline shape; FLOPs counted as 2.5x the forward's
+    (the five products S, dP, dV, dQ, dK; the kernels recompute S twice more)."""
+    q, k, v = inputs.qkv(B, H, S, S, D, seed=0, dtype=torch.bfloat16, device="cuda")
+    do = inputs.normal((B, H, S, D), 0, inputs.TENSOR_OUTLIER, dtype=torch.bfloat16, device="cuda")
+    scale = 1 / math.sqrt(D)
+    o, lse = attn.fwd(q, k, v, causal, scale)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ms, _ = time_launches(lambda: attn.bwd(q, k, v, o, lse, do, causal, scale, dq=dq, dk=dk, dv=dv), steps, warmup)
+    fl = 2.5 * flops(B, H, S, S, D, causal)
+    res = {"B": B, "H": H, "S": S, "D": D, "causal": causal, "ms": round(ms, 4), "tflops": round(fl / ms / 1e9, 1),
+           "pct_peak": round(100 * fl / ms / 1e9 / PEAK_BF16, 1)}
+    del q, k, v, do, o, lse, dq, dk, dv
+    torch.cuda.empty_cache()
+    return res
+
+
 def fp8_point(steps=10, warmup=3):
     """FP8 pipeline on the outlier workload: B=2, H=16, S=8K, D=128, non-causal."""
     B, H, S, D = 2, 16, 8192, 128
@@ -190,7 +207,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["fp8", "decode", "d256", "causal_sweep", "d64_sweep", "varlen"],
+    ap.add_argument("--only", choices=["fp8", "decode", "d256", "causal_sweep", "d64_sweep", "varlen", "bwd"],
                     default=None,
                     help="run just this extra workload and print its JSON (for profiling one kernel family)")
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -225,6 +242,7 @@ def main():
             "d64_sweep": lambda: [bf16_point(16384 // n, 32, n, n, 64, False, steps=st, warmup=wu)
                                   for n in (512, 1024, 2048, 4096, 8192, 16384)],
             "varlen": lambda: [varlen_point(c, steps=st, warmup=wu) for c in (True, False)],
+            "bwd": lambda: [bwd_point(c, steps=st, warmup=wu) for c in (False, True)],
         }
         print(json.dumps({"only": args.only, "result": runs[args.only]()}), flush=True)
         return
@@ -292,6 +310,7 @@ def main():
         extras["decode_32k"] = decode_point()
         extras["fp8_pipeline_8k"] = fp8_point()
         extras["varlen_16k_tokens"] = [varlen_point(True), varlen_point(False)]
+        extras["backward_8k"] = [bwd_point(False), bwd_point(True)]
         out["extras"] = extras
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(B, H, S, D, causal)

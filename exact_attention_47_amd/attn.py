@@ -44,6 +44,7 @@ _SIGS = {
     "attn_fwd_fp8": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i, _i, _vp]),
     "attn_fwd_varlen": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _f, _i, _vp]),
     "rope_hadamard_quant": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp]),
+    "attn_bwd": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i, _vp]),
 }
 
 
@@ -194,6 +195,37 @@ def fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q=None, max_seqle
         total_q, total_k, int(max_seqlen_q), int(max_seqlen_k), D, int(causal), float(scale), _DTYPE[q.dtype],
         st))
     return out, lse
+
+
+def bwd(q, k, v, o, lse, dout, causal=False, scale=None, dq=None, dk=None, dv=None):
+    """(dQ, dK, dV) of attention for [B, H, S, D] tensors, given the forward output O and its LSE."""
+    _need_gpu(q, k, v, o, lse, dout)
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, S, D]")
+    if not (q.dtype == k.dtype == v.dtype == o.dtype == dout.dtype) or q.dtype not in (torch.float16,
+                                                                                         torch.bfloat16):
+        raise ValueError("q, k, v, o, dout must share float16 or bfloat16")
+    B, H, S_q, D = q.shape
+    S_k = k.shape[2]
+    if tuple(k.shape) != (B, H, S_k, D) or tuple(v.shape) != (B, H, S_k, D):
+        raise ValueError("k and v must be [B, H, S_k, D] matching q")
+    if tuple(o.shape) != tuple(q.shape) or tuple(dout.shape) != tuple(q.shape):
+        raise ValueError("o and dout must be like q")
+    if tuple(lse.shape) != (B, H, S_q) or lse.dtype != torch.float32:
+        raise ValueError("lse must be float32 [B, H, S_q]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    _need_gpu(dq, dk, dv)
+    if dq.shape != q.shape or dk.shape != k.shape or dv.shape != v.shape or not (
+            dq.dtype == dk.dtype == dv.dtype == q.dtype):
+        raise ValueError("dq, dk, dv must be like q, k, v")
+    _check("attn_bwd", load().attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
+                                       _ptr(dk), _ptr(dv), B, H, S_q, S_k, D, int(causal), float(scale),
+                                       _DTYPE[q.dtype], _stream(q.device)))
+    return dq, dk, dv
 
 
 def check_args(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, H, S_q, S_k, D, causal, scale, dtype) -> int:

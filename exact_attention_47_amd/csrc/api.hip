@@ -237,6 +237,41 @@ int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float*
   return rc;
 }
 
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+             void* dq, void* dk, void* dv, int B, int H, int S_q, int S_k, int D, int causal, float scale,
+             int dtype, void* stream) {
+  int rc = ATTN_OK;
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) rc = ATTN_ERR_INVALID_ARG;
+  else if (B <= 0 || H <= 0 || S_q <= 0 || S_k <= 0 || D <= 0) rc = ATTN_ERR_INVALID_ARG;
+  else if (dtype != ATTN_F32 && dtype != ATTN_F16 && dtype != ATTN_BF16) rc = ATTN_ERR_INVALID_ARG;
+  else if (causal != 0 && causal != 1) rc = ATTN_ERR_INVALID_ARG;
+  else if (!(scale > 0.0f) || !isfinite(scale)) rc = ATTN_ERR_INVALID_ARG;
+  else if (dtype == ATTN_F32 || (D != 64 && D != 128)) rc = ATTN_ERR_UNSUPPORTED;
+  else if (causal && S_q > S_k) rc = ATTN_ERR_UNSUPPORTED;
+  else if ((long long)B * H * ((S_q > S_k ? S_q : S_k) + 127) / 128 > 0x7fffffffLL) rc = ATTN_ERR_UNSUPPORTED;
+  else if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(dout, 16) ||
+           !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(lse, 4))
+    rc = ATTN_ERR_MISALIGNED;
+  if (rc != ATTN_OK) {
+    say("attn_bwd", rc);
+    return rc;
+  }
+  hipStream_t st = (hipStream_t)stream;
+  void* dd = nullptr;
+  if (hipMallocAsync(&dd, (size_t)B * H * S_q * sizeof(float), st) != hipSuccess) return ATTN_ERR_LAUNCH;
+  attn::BwdArgs a;
+  a.q = q; a.k = k; a.v = v; a.o = o; a.dout = dout; a.lse = lse; a.dd = (float*)dd;
+  a.dq = dq; a.dk = dk; a.dv = dv;
+  a.B = B; a.H = H; a.S_q = S_q; a.S_k = S_k; a.D = D; a.causal = causal; a.dtype = dtype; a.scale = scale;
+  hipError_t e = attn::launch_bwd(a, st);
+  if (hipFreeAsync(dd, st) != hipSuccess && e == hipSuccess) e = hipErrorUnknown;
+  if (e != hipSuccess) {
+    rc = e == hipErrorInvalidValue ? ATTN_ERR_UNSUPPORTED : ATTN_ERR_LAUNCH;
+    say("attn_bwd", rc);
+  }
+  return rc;
+}
+
 int hadamard_quant(const void* x, void* x8, float* scales, const signed char* signs, int B, int H,
                    int S, int D, int block_rows, int apply_hadamard, int in_dtype, void* stream) {
   if (!x || !x8 || !scales || !signs) return ATTN_ERR_INVALID_ARG;

@@ -1,0 +1,396 @@
+// Backward pass of the fused attention on gfx950 matrix cores (bf16 / fp16,
+// D = 64 / 128).
+//
+// The forward pass keeps the row logsumexp so that the backward pass can
+// recompute the probabilities block by block instead of storing them ([GN]
+// "Rueckblick auf den FlashAttention-Ansatz"). With S = scale Q K^T,
+// P = exp(S - LSE), the gradients of O = P V are
+//
+//   dV = P^T dO,  dP = dO V^T,  dS = P * (dP - Dd),  Dd_i = sum_d dO_id O_id,
+//   dQ = scale dS K,  dK = scale dS^T Q.
+//
+// Three launches of one kernel template share the forward kernel's operand
+// layout (a 32-row "outer" block per wave held in registers as the B operand,
+// 32-row "inner" tiles streamed through LDS, accumulators transposed so that
+// one lane owns one outer row):
+//
+//   mode dQ: outer = query rows, inner = keys:  S^T = K Q^T, dP^T = V dO^T,
+//            dQ^T += K^T dS^T
+//   mode dK: outer = keys, inner = query rows:  S = Q K^T,  dP = dO V^T,
+//            dK^T += Q^T dS
+//   mode dV: outer = keys, inner = query rows:  S = Q K^T,  dV^T += dO^T P
+//
+// Splitting dK and dV recomputes S once more (eight products per tile pair
+// instead of five) but keeps each wave under the 256 registers that two waves
+// per SIMD allow, and every gradient is a plain sum in a fixed order: results
+// are deterministic (no atomics). The A operands of the accumulations (K^T,
+// Q^T, dO^T) are read from the staged tiles with ds_read_b64_tr_b16, choosing
+// for each k slot the inner row that the probability fragment holds there,
+// exactly as the forward pass reads V^T. Staged tiles use the K-style XOR
+// swizzle (row reads conflict-free; the transposed reads may conflict).
+//
+// Dd comes from a small first kernel (one row per D/8 lanes, float32 sum).
+#include "common.h"
+#include "kernels.h"
+
+namespace attn {
+
+namespace {
+
+template <typename T> struct BMma;
+template <> struct BMma<__bf16> {
+  typedef v8bf16 frag;
+  static __device__ __forceinline__ v16f mma(frag a, frag b, v16f c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ frag cvt(v8f x) { return __builtin_convertvector(x, v8bf16); }
+};
+template <> struct BMma<_Float16> {
+  typedef v8f16 frag;
+  static __device__ __forceinline__ v16f mma(frag a, frag b, v16f c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ frag cvt(v8f x) { return __builtin_convertvector(x, v8f16); }
+};
+
+constexpr int kDQ = 0, kDK = 1, kDV = 2;
+
+template <int D>
+struct BwdCfg {
+  static constexpr int NW = 4;                  // waves per workgroup
+  static constexpr int NT = NW * 64;
+  static constexpr int BO = NW * 32;            // outer rows per workgroup
+  static constexpr int BI = 32;                 // inner rows per tile
+  static constexpr int DS = D / 16;             // k-steps over D
+  static constexpr int DB = D / 32;             // 32-wide blocks of D
+  static constexpr int RB = 2 * D;              // bytes per row
+  static constexpr int TILE = BI * RB;
+  static constexpr int STAGE = 2 * TILE;        // X then Y
+  static constexpr int NI = TILE / (NT * 16);   // direct loads per thread per tile
+  static constexpr int RPI = 1024 / RB;         // rows per 1 KiB wave load
+  static_assert(TILE % (NT * 16) == 0, "tile must split into 1 KiB wave loads");
+};
+
+template <int D> __device__ __forceinline__ int bswz(int r) { return D == 64 ? (r >> 1) & 7 : r & 15; }
+
+template <typename T>
+__device__ __forceinline__ void load8f(const T* p, float* out) {
+  const uint4 raw = *(const uint4*)p;
+  const T* e = (const T*)&raw;
+#pragma unroll
+  for (int i = 0; i < 8; i++) out[i] = (float)e[i];
+}
+
+// Dd[row] = sum_d dO[row][d] * O[row][d], float32, D/8 lanes per row
+template <typename T, int D>
+__global__ void __launch_bounds__(256) bwd_dot_kernel(const T* __restrict__ O, const T* __restrict__ dO,
+                                                       float* __restrict__ Dd, long rows)
+{
+  constexpr int LPR = D / 8;
+  const long g = (long)blockIdx.x * 256 + threadIdx.x;
+  const long row = g / LPR;
+  const int part = (int)(g % LPR);
+  float acc = 0.0f;
+  if (row < rows) {
+    float a[8], b[8];
+    load8f(O + row * D + part * 8, a);
+    load8f(dO + row * D + part * 8, b);
+#pragma unroll
+    for (int i = 0; i < 8; i++) acc += a[i] * b[i];
+  }
+#pragma unroll
+  for (int off = LPR / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
+  if (row < rows && part == 0) Dd[row] = acc;
+}
+
+template <typename T, int D, int MODE, bool CAUSAL>
+__global__ void __launch_bounds__(256)
+__attribute__((amdgpu_waves_per_eu(2, 2)))
+bwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
+           const T* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dd,
+           T* __restrict__ Gout, int BH, int S_q, int S_k, int n_ot, float c, float gscale)
+{
+  using C = BwdCfg<D>;
+  using M = BMma<T>;
+  typedef typename M::frag frag;
+  constexpr bool DQ = MODE == kDQ;
+  constexpr bool TWO = MODE != kDV;             // second product dP needed
+  __shared__ __attribute__((aligned(1024))) char st0[C::STAGE];
+  __shared__ __attribute__((aligned(1024))) char st1[C::STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hh = lane >> 5;
+  const int nn = lane & 31;
+
+  const int work = xcd_swizzle(blockIdx.x, BH * n_ot);
+  int ot = work % n_ot;
+  const int bh = work / n_ot;
+  if (CAUSAL && DQ) ot = n_ot - 1 - ot;        // late query tiles have the most keys
+  const int S_o = DQ ? S_q : S_k;
+  const int S_i = DQ ? S_k : S_q;
+  const int o0 = ot * C::BO;
+  const int wr0 = o0 + wave * 32;               // this wave's outer rows
+  const int diag = S_k - S_q;                   // key j allowed for query i iff j <= i + diag
+
+  // inner rows that any outer row of the workgroup can see
+  int i_lo = 0, i_hi = S_i;
+  if (CAUSAL) {
+    if (DQ) i_hi = min(S_k, o0 + C::BO - 1 + diag + 1);
+    else i_lo = max(0, o0 - diag);
+  }
+  const int t_begin = i_lo / C::BI;
+  const int t_end = i_hi > i_lo ? (i_hi + C::BI - 1) / C::BI : t_begin;
+
+  const size_t qo = (size_t)bh * S_q * D, ko = (size_t)bh * S_k * D;
+  const T* O1 = DQ ? Q + qo : K + ko;           // outer, first product
+  const T* O2 = DQ ? dO + qo : V + ko;          // outer, second product
+  const T* Xg = DQ ? K + ko : Q + qo;           // inner, first product (and dQ / dK accumulation)
+  const T* Yg = DQ ? V + ko : dO + qo;          // inner, second product (and dV accumulation)
+  const float* lseh = LSE + (size_t)bh * S_q;
+  const float* ddh = Dd + (size_t)bh * S_q;
+
+  // outer rows as B operands: lane (h, n) holds row wr0+n, d = 16 ds + 8 h .. +7
+  frag of1[C::DS], of2[TWO ? C::DS : 1];
+  {
+    const int r = wr0 + nn;
+#pragma unroll
+    for (int ds = 0; ds < C::DS; ds++) {
+      if (r < S_o) {
+        of1[ds] = *(const frag*)(O1 + (size_t)r * D + ds * 16 + 8 * hh);
+        if constexpr (TWO) of2[ds] = *(const frag*)(O2 + (size_t)r * D + ds * 16 + 8 * hh);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; e++) {
+          of1[ds][e] = (T)0.0f;
+          if constexpr (TWO) of2[ds][e] = (T)0.0f;
+        }
+      }
+    }
+  }
+  // per-lane scalars of the outer query row (mode dQ)
+  float lse2_o = 0.0f, dd_o = 0.0f;
+  if (DQ && wr0 + nn < S_q) {
+    lse2_o = lseh[wr0 + nn] * kLog2e;
+    dd_o = ddh[wr0 + nn];
+  }
+
+  // stage t: X rows 32t.., Y rows 32t.. (buffer loads; rows past the end read 0)
+  const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc((void*)Xg, (short)0, S_i * C::RB, 0x00020000);
+  const __amdgpu_buffer_rsrc_t yrs = __builtin_amdgcn_make_buffer_rsrc((void*)Yg, (short)0, S_i * C::RB, 0x00020000);
+  const int dma_rsub = (lane * 16) / C::RB;
+  const int dma_u = ((lane * 16) % C::RB) / 16;
+  // (offsets and destinations go through locals: a target builtin with
+  // template-dependent argument expressions is dropped from the host pass)
+  auto issue_stage = [&](int t, char* base) {
+#pragma unroll
+    for (int i = 0; i < C::NI; i++) {
+      const int blk = i * C::NW + wave;
+      const int r = blk * C::RPI + dma_rsub;
+      const int off = (t * C::BI + r) * C::RB + ((dma_u ^ bswz<D>(r)) * 16);
+      char* xd = base + blk * 1024;
+      char* yd = base + C::TILE + blk * 1024;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(xrs, (__attribute__((address_space(3))) void*)xd, 16, off, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(yrs, (__attribute__((address_space(3))) void*)yd, 16, off, 0, 0, 0);
+    }
+  };
+
+  // LDS read offsets: row reads (A of the two products) and transposed reads
+  // (A of the accumulation)
+  constexpr int NKR = C::DS < 8 ? C::DS : 8;
+  const int xk = bswz<D>(nn);
+  int k_rd[NKR];
+#pragma unroll
+  for (int ds = 0; ds < NKR; ds++) k_rd[ds] = nn * C::RB + (((2 * ds + hh) ^ xk) * 16);
+  const int g = lane >> 4, jj = lane & 15;
+  const int vrow = 4 * hh + (jj >> 2);          // inner row = vrow + 16 ks + 8 part
+  const int x0 = bswz<D>(vrow), x1 = bswz<D>(vrow + 8);
+  int tr_lo[C::DB], tr_hi[C::DB];
+#pragma unroll
+  for (int db = 0; db < C::DB; db++) {
+    const int chunk = 4 * db + 2 * (g & 1) + ((jj & 3) >> 1);
+    tr_lo[db] = vrow * C::RB + ((chunk ^ x0) * 16) + 8 * (jj & 1);
+    tr_hi[db] = (vrow + 8) * C::RB + ((chunk ^ x1) * 16) + 8 * (jj & 1);
+  }
+
+  v16f acc[C::DB];
+#pragma unroll
+  for (int db = 0; db < C::DB; db++)
+#pragma unroll
+    for (int e = 0; e < 16; e++) acc[db][e] = 0.0f;
+
+  auto barrier = [] {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+  };
+
+  auto step = [&](int t, const char* st) {
+    const char* xs = st;
+    const char* ys = st + C::TILE;
+    // C[inner 32 x outer 32] = X_tile O1^T (lane (h, n): outer row n, inner rows 8i + 4h + j)
+    v16f s;
+#pragma unroll
+    for (int e = 0; e < 16; e++) s[e] = 0.0f;
+#pragma unroll
+    for (int ds = 0; ds < C::DS; ds++) {
+      const frag a = *(const frag*)(xs + k_rd[ds % NKR] + (ds / NKR) * 256);
+      s = M::mma(a, of1[ds], s);
+    }
+    v16f dp = {};
+    if constexpr (TWO) {
+#pragma unroll
+      for (int e = 0; e < 16; e++) dp[e] = 0.0f;
+#pragma unroll
+      for (int ds = 0; ds < C::DS; ds++) {
+        const frag a = *(const frag*)(ys + k_rd[ds % NKR] + (ds / NKR) * 256);
+        dp = M::mma(a, of2[ds], dp);
+      }
+    }
+    // probabilities (and dS), masked where the key is outside the range or
+    // after the causal limit
+    const int orow = wr0 + nn;
+    float gv[16];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      float l4[4], d4[4];
+      const int ir0 = t * C::BI + 8 * i + 4 * hh;   // inner rows ir0 .. ir0+3
+      if (!DQ) {
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+          const int ir = ir0 + j;
+          l4[j] = ir < S_q ? lseh[ir] * kLog2e : 0.0f;
+          d4[j] = (MODE == kDK && ir < S_q) ? ddh[ir] : 0.0f;
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        const int e = 4 * i + j;
+        const int ir = ir0 + j;
+        const int query = DQ ? orow : ir;
+        const int key = DQ ? ir : orow;
+        const bool ok = query < S_q && key < S_k && (!CAUSAL || key <= query + diag);
+        const float l2 = DQ ? lse2_o : l4[j];
+        const float p = ok ? fast_exp2(__builtin_fmaf(s[e], c, -l2)) : 0.0f;
+        if (MODE == kDV) {
+          gv[e] = p;
+        } else {
+          const float ddv = DQ ? dd_o : d4[j];
+          gv[e] = p * (dp[e] - ddv);
+        }
+      }
+    }
+    frag gf[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ks++) {
+      v8f w;
+#pragma unroll
+      for (int e = 0; e < 8; e++) w[e] = gv[8 * ks + e];
+      gf[ks] = M::cvt(w);
+    }
+    // acc^T[d x outer] += Z^T[d x inner] G[inner x outer], Z = X (dQ, dK) or Y (dV)
+    const char* zs = MODE == kDV ? ys : xs;
+#pragma unroll
+    for (int ks = 0; ks < 2; ks++)
+#pragma unroll
+      for (int db = 0; db < C::DB; db++) {
+        const char* za = zs + 16 * ks * C::RB;
+        v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(za + tr_lo[db]));
+        v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(za + tr_hi[db]));
+        const frag a = __builtin_bit_cast(frag, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        acc[db] = M::mma(a, gf[ks], acc[db]);
+      }
+  };
+
+  if (t_end > t_begin) {
+    issue_stage(t_begin, st0);
+    __builtin_amdgcn_s_waitcnt(0x0070 | 0x0F00);
+    int t = t_begin;
+    for (; t + 1 < t_end; t += 2) {
+      barrier();
+      issue_stage(t + 1, st1);
+      step(t, st0);
+      __builtin_amdgcn_s_waitcnt(0x0070 | 0x0F00);
+      barrier();
+      if (t + 2 < t_end) issue_stage(t + 2, st0);
+      step(t + 1, st1);
+      __builtin_amdgcn_s_waitcnt(0x0070 | 0x0F00);
+    }
+    if (t < t_end) {
+      barrier();
+      step(t, st0);
+    }
+  }
+
+  // store the gradient rows of this wave: lane (h, n) holds row wr0+n,
+  // columns 32 db + 8 i + 4 h + j
+  const int r = wr0 + nn;
+  if (r < S_o) {
+    T* grow = Gout + (size_t)bh * S_o * D + (size_t)r * D;
+#pragma unroll
+    for (int db = 0; db < C::DB; db++)
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        typedef T v4t __attribute__((ext_vector_type(4)));
+        v4t w;
+#pragma unroll
+        for (int j = 0; j < 4; j++) w[j] = (T)(acc[db][4 * i + j] * gscale);
+        *(v4t*)(grow + db * 32 + 8 * i + 4 * hh) = w;
+      }
+  }
+}
+
+template <typename T, int D, int MODE>
+hipError_t launch_mode(const BwdArgs& a, hipStream_t st) {
+  using C = BwdCfg<D>;
+  const int S_o = MODE == kDQ ? a.S_q : a.S_k;
+  const int n_ot = (S_o + C::BO - 1) / C::BO;
+  const dim3 grid((unsigned)(a.B * a.H * n_ot));
+  T* out = (T*)(MODE == kDQ ? a.dq : MODE == kDK ? a.dk : a.dv);
+  const float gscale = MODE == kDV ? 1.0f : a.scale;
+  if (a.causal)
+    hipLaunchKernelGGL((bwd_kernel<T, D, MODE, true>), grid, dim3(C::NT), 0, st, (const T*)a.q, (const T*)a.k,
+                       (const T*)a.v, (const T*)a.dout, a.lse, a.dd, out, a.B * a.H, a.S_q, a.S_k, n_ot,
+                       a.scale * kLog2e, gscale);
+  else
+    hipLaunchKernelGGL((bwd_kernel<T, D, MODE, false>), grid, dim3(C::NT), 0, st, (const T*)a.q, (const T*)a.k,
+                       (const T*)a.v, (const T*)a.dout, a.lse, a.dd, out, a.B * a.H, a.S_q, a.S_k, n_ot,
+                       a.scale * kLog2e, gscale);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch_d(const BwdArgs& a, hipStream_t st) {
+  // K and V (and Q, dO) are addressed through 32-bit buffer offsets
+  if ((long long)(a.S_k > a.S_q ? a.S_k : a.S_q) * 2 * D + 2LL * 32 * 2 * D > 0x7fffffffLL) return hipErrorInvalidValue;
+  const long rows = (long)a.B * a.H * a.S_q;
+  const long threads = rows * (D / 8);
+  hipLaunchKernelGGL((bwd_dot_kernel<T, D>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st,
+                     (const T*)a.o, (const T*)a.dout, a.dd, rows);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if ((e = launch_mode<T, D, kDQ>(a, st)) != hipSuccess) return e;
+  if ((e = launch_mode<T, D, kDK>(a, st)) != hipSuccess) return e;
+  return launch_mode<T, D, kDV>(a, st);
+}
+
+template <typename T>
+hipError_t launch_t(const BwdArgs& a, hipStream_t st) {
+  switch (a.D) {
+    case 64: return launch_d<T, 64>(a, st);
+    case 128: return launch_d<T, 128>(a, st);
+  }
+  return hipErrorNotSupported;
+}
+
+}  // namespace
+
+hipError_t launch_bwd(const BwdArgs& a, hipStream_t st) {
+  if (a.dtype == 2) return launch_t<__bf16>(a, st);
+  return launch_t<_Float16>(a, st);
+}
+
+}  // namespace attn

@@ -32,6 +32,25 @@ hipError_t launch_fwd_mfma(const FwdArgs& a, hipStream_t st);
 int mfma_rows_per_block(int D);
 int mfma_keys_per_tile(int D);
 
+// backward pass (bf16 / fp16, D = 64 / 128): Dd, then dQ, dK, dV
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;    // [B*H][S_q], natural log, from the forward pass
+  float* dd;           // workspace [B*H][S_q]: rowsum(dO * O)
+  void* dq;
+  void* dk;
+  void* dv;
+  int B, H, S_q, S_k, D;
+  int causal;
+  int dtype;
+  float scale;
+};
+hipError_t launch_bwd(const BwdArgs& a, hipStream_t st);
+
 // packed (variable-length) batches on the bf16 / fp16 kernel, D = 64 / 128
 hipError_t launch_fwd_varlen(const FwdArgs& a, hipStream_t st);
 

@@ -136,6 +136,28 @@ int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float*
                     int total_q, int total_k, int max_seqlen_q, int max_seqlen_k, int D,
                     int causal, float scale, int dtype, void* stream);
 
+/*
+ * attn_bwd -- gradients of attn_fwd's output: dQ, dK, dV from Q, K, V, the
+ * forward output O and its LSE, and dO. The forward pass keeps the LSE so
+ * that the backward pass recomputes the probabilities instead of storing them
+ * ([GN] "Rueckblick auf den FlashAttention-Ansatz").
+ *
+ *   q, o, dout, dq  [B, H, S_q, D];  k, v, dk, dv  [B, H, S_k, D]  (dtype)
+ *   lse             [B, H, S_q] float32, as written by attn_fwd
+ *   scale, causal   as given to attn_fwd
+ *
+ * dQ = scale dS K, dK = scale dS^T Q, dV = P^T dO with P = exp(scale Q K^T - LSE)
+ * (masked like the forward pass), dS = P * (dO V^T - rowsum(dO * O)). dtype is
+ * ATTN_BF16 or ATTN_F16 and D is 64 or 128 (otherwise ATTN_ERR_UNSUPPORTED);
+ * causal with S_q > S_k is ATTN_ERR_UNSUPPORTED as in attn_fwd. Accumulation
+ * is float32 in a fixed order (deterministic); the gradients are rounded to
+ * dtype. A float32 scratch of B*H*S_q values comes from the stream-ordered
+ * allocator on `stream` and is released on it.
+ */
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+             const void* dout, void* dq, void* dk, void* dv, int B, int H, int S_q, int S_k,
+             int D, int causal, float scale, int dtype, void* stream);
+
 /* Bytes of workspace attn_fwd_ex needs for these sizes and split request
  * (0 when the effective split count is 1). num_splits = 0 means "automatic". */
 size_t attn_fwd_workspace_size(int B, int H, int S_q, int S_k, int D, int num_splits);
