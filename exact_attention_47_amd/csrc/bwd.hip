@@ -65,7 +65,7 @@ struct BwdCfg {
   static constexpr int DB = D / 32;             // 32-wide blocks of D
   static constexpr int RB = 2 * D;              // bytes per row
   static constexpr int TILE = BI * RB;
-  static constexpr int STAGE = 2 * TILE;        // X then Y
+  static constexpr int STAGE = 2 * TILE + 512;  // X, Y, then 64 LSE and 64 Dd values (inner = queries)
   static constexpr int NI = TILE / (NT * 16);   // direct loads per thread per tile
   static constexpr int RPI = 1024 / RB;         // rows per 1 KiB wave load
   static_assert(TILE % (NT * 16) == 0, "tile must split into 1 KiB wave loads");
@@ -105,7 +105,7 @@ __global__ void __launch_bounds__(256) bwd_dot_kernel(const T* __restrict__ O, c
 
 template <typename T, int D, int MODE, bool CAUSAL>
 __global__ void __launch_bounds__(256)
-__attribute__((amdgpu_waves_per_eu(2, 2)))
+__attribute__((amdgpu_waves_per_eu(MODE == 2 ? 3 : 2, MODE == 2 ? 3 : 2)))
 bwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
            const T* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dd,
            T* __restrict__ Gout, int BH, int S_q, int S_k, int n_ot, float c, float gscale)
@@ -183,7 +183,19 @@ bwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict
   const int dma_u = ((lane * 16) % C::RB) / 16;
   // (offsets and destinations go through locals: a target builtin with
   // template-dependent argument expressions is dropped from the host pass)
+  // (inner = queries: wave 0 also stages the tile's LSE and Dd values, 64
+  // rows per instruction, rows past S_q read 0)
+  const __amdgpu_buffer_rsrc_t lrs = __builtin_amdgcn_make_buffer_rsrc((void*)lseh, (short)0, S_q * 4, 0x00020000);
+  const __amdgpu_buffer_rsrc_t drs = __builtin_amdgcn_make_buffer_rsrc((void*)ddh, (short)0, S_q * 4, 0x00020000);
   auto issue_stage = [&](int t, char* base) {
+    if (!DQ && wave == 0) {
+      char* ld = base + 2 * C::TILE;
+      char* dd = base + 2 * C::TILE + 256;
+      const int off = (t * C::BI + lane) * 4;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(lrs, (__attribute__((address_space(3))) void*)ld, 4, off, 0, 0, 0);
+      if (MODE == kDK)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(drs, (__attribute__((address_space(3))) void*)dd, 4, off, 0, 0, 0);
+    }
 #pragma unroll
     for (int i = 0; i < C::NI; i++) {
       const int blk = i * C::NW + wave;
@@ -259,11 +271,13 @@ bwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict
       float l4[4], d4[4];
       const int ir0 = t * C::BI + 8 * i + 4 * hh;   // inner rows ir0 .. ir0+3
       if (!DQ) {
-#pragma unroll
-        for (int j = 0; j < 4; j++) {
-          const int ir = ir0 + j;
-          l4[j] = ir < S_q ? lseh[ir] * kLog2e : 0.0f;
-          d4[j] = (MODE == kDK && ir < S_q) ? ddh[ir] : 0.0f;
+        const float4 lv = *(const float4*)(st + 2 * C::TILE + (8 * i + 4 * hh) * 4);
+        l4[0] = lv.x * kLog2e; l4[1] = lv.y * kLog2e; l4[2] = lv.z * kLog2e; l4[3] = lv.w * kLog2e;
+        if (MODE == kDK) {
+          const float4 dv4 = *(const float4*)(st + 2 * C::TILE + 256 + (8 * i + 4 * hh) * 4);
+          d4[0] = dv4.x; d4[1] = dv4.y; d4[2] = dv4.z; d4[3] = dv4.w;
+        } else {
+          d4[0] = d4[1] = d4[2] = d4[3] = 0.0f;
         }
       }
 #pragma unroll
