@@ -26,8 +26,8 @@
 // are deterministic (no atomics). The A operands of the accumulations (K^T,
 // Q^T, dO^T) are read from the staged tiles with ds_read_b64_tr_b16, choosing
 // for each k slot the inner row that the probability fragment holds there,
-// exactly as the forward pass reads V^T. Staged tiles use the K-style XOR
-// swizzle (row reads conflict-free; the transposed reads may conflict).
+// exactly as the forward pass reads V^T. Staged tiles use an XOR swizzle that
+// suits both read patterns (see bswz).
 //
 // Dd comes from a small first kernel (one row per D/8 lanes, float32 sum).
 #include "common.h"
@@ -71,7 +71,15 @@ struct BwdCfg {
   static_assert(TILE % (NT * 16) == 0, "tile must split into 1 KiB wave loads");
 };
 
-template <int D> __device__ __forceinline__ int bswz(int r) { return D == 64 ? (r >> 1) & 7 : r & 15; }
+// Row-dependent 16-byte-chunk XOR swizzle of the staged tiles, which are read
+// both by rows (16 lanes: one chunk of 16 consecutive rows) and transposed
+// (32 lanes: four chunks of 4 consecutive rows). At D = 128 (16 chunks per
+// row) ((r & 3) << 2) | ((r >> 2) & 3) gives 16 consecutive rows 16 distinct
+// values and 4 aligned rows 4 distinct quarters, so both patterns touch
+// every bank once; D = 64 keeps the row-read swizzle of the forward pass.
+template <int D> __device__ __forceinline__ int bswz(int r) {
+  return D == 64 ? (r >> 1) & 7 : ((r & 3) << 2) | ((r >> 2) & 3);
+}
 
 template <typename T>
 __device__ __forceinline__ void load8f(const T* p, float* out) {
