@@ -327,23 +327,28 @@ bwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict
       }
   };
 
+  // Causal dK and dV: each workgroup's inner range starts at its own diagonal
+  // and ends at the last query tile. Walked backwards from the end, the
+  // workgroups of one head read the same query tiles at about the same time
+  // (one moving window in L2 instead of one per starting point).
+  auto tile = [&](int u) { return (CAUSAL && !DQ) ? t_begin + t_end - 1 - u : u; };
   if (t_end > t_begin) {
-    issue_stage(t_begin, st0);
+    issue_stage(tile(t_begin), st0);
     __builtin_amdgcn_s_waitcnt(0x0070 | 0x0F00);
     int t = t_begin;
     for (; t + 1 < t_end; t += 2) {
       barrier();
-      issue_stage(t + 1, st1);
-      step(t, st0);
+      issue_stage(tile(t + 1), st1);
+      step(tile(t), st0);
       __builtin_amdgcn_s_waitcnt(0x0070 | 0x0F00);
       barrier();
-      if (t + 2 < t_end) issue_stage(t + 2, st0);
-      step(t + 1, st1);
+      if (t + 2 < t_end) issue_stage(tile(t + 2), st0);
+      step(tile(t + 1), st1);
       __builtin_amdgcn_s_waitcnt(0x0070 | 0x0F00);
     }
     if (t < t_end) {
       barrier();
-      step(t, st0);
+      step(tile(t), st0);
     }
   }
 
