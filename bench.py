@@ -76,18 +76,37 @@ def time_launches(fn, steps, warmup):
     return sum(per) / len(per), min(per)
 
 
-def bf16_point(B, H, S_q, S_k, D, causal, steps=10, warmup=3, seed=0):
+def bf16_point(B, H, S_q, S_k, D, causal, steps=10, warmup=3, seed=0, persistent=None):
+    """One bf16 forward workload; persistent=n times attn_fwd_persistent on n workgroups (0 = one per CU)."""
     q, k, v = inputs.qkv(B, H, S_q, S_k, D, seed=seed, dtype=torch.bfloat16, device="cuda")
     o = torch.empty_like(q)
     lse = torch.empty((B, H, S_q), dtype=torch.float32, device="cuda")
     scale = 1 / math.sqrt(D)
-    ms, ms_min = time_launches(lambda: attn.fwd(q, k, v, causal, scale, out=o, lse=lse), steps, warmup)
+    if persistent is None:
+        fn = lambda: attn.fwd(q, k, v, causal, scale, out=o, lse=lse)
+    else:
+        fn = lambda: attn.fwd_persistent(q, k, v, causal, scale, out=o, lse=lse, num_workgroups=persistent)
+    ms, ms_min = time_launches(fn, steps, warmup)
     fl = flops(B, H, S_q, S_k, D, causal)
     res = {"B": B, "H": H, "S_q": S_q, "S_k": S_k, "D": D, "causal": causal, "ms": round(ms, 4),
            "tflops": round(fl / ms / 1e9, 1), "pct_peak": round(100 * fl / ms / 1e9 / PEAK_BF16, 1)}
+    if persistent is not None:
+        res["persistent_workgroups"] = persistent
     del q, k, v, o, lse
     torch.cuda.empty_cache()
     return res
+
+
+def persistent_points(steps=10, warmup=3):
+    """Causal D128 at 8K and 16K tokens per batch: hardware-dealt grid vs the persistent grid on every CU
+    and on a quarter of them."""
+    out = []
+    bf16_point(2, 16, 8192, 8192, 128, True, steps=steps, warmup=warmup)   # untimed: clocks up before the pairs
+    for B, S in ((2, 8192), (1, 16384)):
+        out.append(bf16_point(B, 16, S, S, 128, True, steps=steps, warmup=warmup))
+        for n in (0, 64):
+            out.append(bf16_point(B, 16, S, S, 128, True, steps=steps, warmup=warmup, persistent=n))
+    return out
 
 
 def decode_point(steps=10, warmup=3):
@@ -207,7 +226,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["fp8", "decode", "d256", "causal_sweep", "d64_sweep", "varlen", "bwd"],
+    ap.add_argument("--only", choices=["fp8", "decode", "d256", "causal_sweep", "d64_sweep", "varlen", "bwd",
+                                       "persistent"],
                     default=None,
                     help="run just this extra workload and print its JSON (for profiling one kernel family)")
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -243,6 +263,7 @@ def main():
                                   for n in (512, 1024, 2048, 4096, 8192, 16384)],
             "varlen": lambda: [varlen_point(c, steps=st, warmup=wu) for c in (True, False)],
             "bwd": lambda: [bwd_point(c, steps=st, warmup=wu) for c in (False, True)],
+            "persistent": lambda: persistent_points(steps=st, warmup=wu),
         }
         print(json.dumps({"only": args.only, "result": runs[args.only]()}), flush=True)
         return
@@ -311,6 +332,7 @@ def main():
         extras["fp8_pipeline_8k"] = fp8_point()
         extras["varlen_16k_tokens"] = [varlen_point(True), varlen_point(False)]
         extras["backward_8k"] = [bwd_point(False), bwd_point(True)]
+        extras["persistent_causal"] = persistent_points()
         out["extras"] = extras
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(B, H, S, D, causal)

@@ -43,6 +43,7 @@ _SIGS = {
     "quant_per_tensor": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp]),
     "attn_fwd_fp8": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i, _i, _vp]),
     "attn_fwd_varlen": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _f, _i, _vp]),
+    "attn_fwd_persistent": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i, _i, _vp]),
     "rope_hadamard_quant": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp]),
     "attn_bwd": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i, _vp]),
 }
@@ -138,6 +139,33 @@ def fwd(q, k, v, causal=False, scale=None, out=None, lse=None, num_splits=None, 
             workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
         wsz = 0 if workspace is None else workspace.numel() * workspace.element_size()
         _check("attn_fwd_ex", lib.attn_fwd_ex(*args, int(num_splits), _ptr(workspace), wsz, st))
+    return out, lse
+
+
+def fwd_persistent(q, k, v, causal=False, scale=None, out=None, lse=None, num_workgroups=0):
+    """``fwd`` on a persistent grid of ``num_workgroups`` workgroups (0 = one per CU).
+
+    bf16 / fp16, D 64 or 128, no key-range split; same outputs as ``fwd``.
+    """
+    _need_gpu(q, k, v)
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, S, D]")
+    if not (q.dtype == k.dtype == v.dtype) or q.dtype not in _DTYPE:
+        raise ValueError("q, k, v must share one of float32/float16/bfloat16")
+    B, H, S_q, D = q.shape
+    S_k = k.shape[2]
+    if tuple(k.shape) != (B, H, S_k, D) or tuple(v.shape) != (B, H, S_k, D):
+        raise ValueError("k and v must be [B, H, S_k, D] matching q")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, S_q), dtype=torch.float32, device=q.device)
+    _need_gpu(out, lse)
+    _check("attn_fwd_persistent", load().attn_fwd_persistent(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, S_q, S_k, D, int(causal), float(scale),
+        _DTYPE[q.dtype], int(num_workgroups), _stream(q.device)))
     return out, lse
 
 

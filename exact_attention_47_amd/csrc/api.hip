@@ -192,6 +192,43 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse
   return rc;
 }
 
+int attn_fwd_persistent(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                        int S_q, int S_k, int D, int causal, float scale, int dtype, int num_workgroups,
+                        void* stream) {
+  int rc = check_args(q, k, v, o, lse, B, H, S_q, S_k, D, causal, scale, dtype);
+  if (rc == ATTN_OK && num_workgroups < 0) rc = ATTN_ERR_INVALID_ARG;
+  if (rc == ATTN_OK && (dtype == ATTN_F32 || (D != 64 && D != 128))) rc = ATTN_ERR_UNSUPPORTED;
+  int n_cu = 0;
+  if (rc == ATTN_OK) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n_cu <= 0)
+      rc = ATTN_ERR_LAUNCH;
+  }
+  // one workgroup per CU at most: the kernel's workgroup fills a CU, so a
+  // larger grid would no longer be resident at once
+  if (rc == ATTN_OK && num_workgroups > n_cu) rc = ATTN_ERR_INVALID_ARG;
+  if (rc != ATTN_OK) {
+    say("attn_fwd_persistent", rc);
+    return rc;
+  }
+  attn::FwdArgs a;
+  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
+  a.B = B; a.H = H; a.S_q = S_q; a.S_k = S_k; a.D = D;
+  a.causal = causal; a.dtype = dtype;
+  a.n_split = 1; a.keys_per_split = 0;
+  a.c = scale * attn::kLog2e;
+  a.opart = nullptr; a.lpart = nullptr;
+  const hipError_t e = attn::launch_fwd_persistent(a, num_workgroups > 0 ? num_workgroups : n_cu,
+                                                   (hipStream_t)stream);
+  if (e != hipSuccess) {
+    if (verbose()) fprintf(stderr, "[attn] launch failed: %s\n", hipGetErrorString(e));
+    say("attn_fwd_persistent", ATTN_ERR_LAUNCH);
+    return ATTN_ERR_LAUNCH;
+  }
+  return ATTN_OK;
+}
+
 int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
                     const int* cu_seqlens_q, const int* cu_seqlens_k, int B, int H, int total_q,
                     int total_k, int max_seqlen_q, int max_seqlen_k, int D, int causal, float scale,

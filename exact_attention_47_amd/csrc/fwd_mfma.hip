@@ -91,7 +91,7 @@ template <int D> __device__ __forceinline__ int v_swz(int r) { return D == 64 ? 
 constexpr float kTau = 8.0f;   // lazy-rescale threshold, log2 domain
 constexpr int kVmcnt0 = 0x0070 | 0x0F00;   // s_waitcnt vmcnt(0), other counters unconstrained
 
-template <typename T, int D, int BN, bool CAUSAL, bool SPLIT, bool VARLEN>
+template <typename T, int D, int BN, bool CAUSAL, bool SPLIT, bool VARLEN, bool PERSIST>
 __global__ void __launch_bounds__(512)
 __attribute__((amdgpu_waves_per_eu(2, 2)))
 fwd_mfma_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
@@ -101,6 +101,7 @@ fwd_mfma_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
                 const int* __restrict__ cu_q, const int* __restrict__ cu_k, int H, int total_q)
 {
   static_assert(!(VARLEN && SPLIT), "packed batches run unsplit");
+  static_assert(!(PERSIST && (VARLEN || SPLIT)), "the persistent grid runs dense, unsplit work");
   using C = FwdCfg<D, BN>;
   using M = Mma<T>;
   typedef typename M::frag frag;
@@ -113,9 +114,33 @@ fwd_mfma_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
   const int hh = lane >> 5;        // lane half
   const int nn = lane & 31;        // query column owned by this lane
 
+  // A persistent grid (PERSIST) runs this body once per work item it is
+  // dealt; otherwise there is one workgroup per item and one pass.
+  for (int it = 0;; it++) {
   // ---- which (b*h, q tile, split) this workgroup computes
   int split, qt, bh;
-  if (!VARLEN && (SPLIT || !CAUSAL)) {
+  if (PERSIST) {
+    // Fixed grid of G workgroups (at most one per CU, all resident). The
+    // items, heaviest query tiles first, are dealt in a snake: on even
+    // rounds workgroup j takes the j-th item of the round, on odd rounds the
+    // (G-1-j)-th, so the heavy and light causal tiles pair up and every
+    // workgroup gets about the same number of keys. When B*H and G are
+    // multiples of 8 the deal runs per XCD (workgroup g sits on XCD g % 8)
+    // over the heads of that XCD only, so a head's tiles share one L2.
+    const int G = gridDim.x;
+    const bool per_xcd = (BH & 7) == 0 && (G & 7) == 0;
+    const int x = per_xcd ? blockIdx.x & 7 : 0;
+    const int j = per_xcd ? blockIdx.x >> 3 : blockIdx.x;
+    const int gx = per_xcd ? G >> 3 : G;
+    const int nbh = per_xcd ? BH >> 3 : BH;
+    const long long i = (long long)it * gx + ((it & 1) ? gx - 1 - j : j);
+    if (i >= (long long)nbh * n_qt) break;
+    const int level = (int)(i / nbh);
+    const int hsel = (int)(i % nbh);
+    bh = per_xcd ? x + 8 * hsel : hsel;
+    qt = n_qt - 1 - level;
+    split = 0;
+  } else if (!VARLEN && (SPLIT || !CAUSAL)) {
     const int n_work = BH * n_qt * n_split;
     int work = xcd_swizzle(blockIdx.x, n_work);
     split = work % n_split;
@@ -462,6 +487,10 @@ fwd_mfma_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
       if (hh == 0) Lpart[prow] = lse;
     }
   }
+  // Persistent: every wave has passed the loop's last barrier after its last
+  // LDS read, so the next item's first stage may overwrite the buffers.
+  if (!PERSIST) break;
+  }
 }
 
 // ---------------------------------------------------------------- launchers
@@ -478,15 +507,16 @@ template <int D> struct Shape;
 template <> struct Shape<64> { static constexpr int BN = FWD_D64_BN; };
 template <> struct Shape<128> { static constexpr int BN = FWD_D128_BN; };
 
-template <typename T, int D, bool CAUSAL, bool SPLIT, bool VARLEN = false>
-static hipError_t launch_one(const FwdArgs& a, hipStream_t st) {
+template <typename T, int D, bool CAUSAL, bool SPLIT, bool VARLEN = false, bool PERSIST = false>
+static hipError_t launch_one(const FwdArgs& a, hipStream_t st, int n_wg = 0) {
   using C = FwdCfg<D, Shape<D>::BN>;
   // 32-bit buffer offsets (packed rows: S_k is the longest sequence's length)
   const long long row_bytes = VARLEN ? (long long)a.H * C::RB : C::RB;
   if ((long long)(a.S_k + C::BN) * row_bytes > 0x7fffffffLL) return hipErrorInvalidValue;
   const int n_qt = (a.S_q + C::BM - 1) / C::BM;
   const int n_work = a.B * a.H * n_qt * a.n_split;
-  hipLaunchKernelGGL((fwd_mfma_kernel<T, D, Shape<D>::BN, CAUSAL, SPLIT, VARLEN>), dim3(n_work), dim3(C::NT), 0,
+  const int grid = PERSIST ? (n_wg < n_work ? n_wg : n_work) : n_work;
+  hipLaunchKernelGGL((fwd_mfma_kernel<T, D, Shape<D>::BN, CAUSAL, SPLIT, VARLEN, PERSIST>), dim3(grid), dim3(C::NT), 0,
                      st, (const T*)a.q, (const T*)a.k, (const T*)a.v, (T*)a.o, a.lse, a.opart, a.lpart,
                      a.B * a.H, a.S_q, a.S_k, n_qt, a.n_split, a.keys_per_split, a.c, a.cu_q, a.cu_k, a.H,
                      a.total_q);
@@ -526,6 +556,23 @@ static hipError_t launch_varlen_t(const FwdArgs& a, hipStream_t st) {
 hipError_t launch_fwd_varlen(const FwdArgs& a, hipStream_t st) {
   if (a.dtype == 2) return launch_varlen_t<__bf16>(a, st);
   return launch_varlen_t<_Float16>(a, st);
+}
+
+template <typename T>
+static hipError_t launch_persistent_t(const FwdArgs& a, int n_wg, hipStream_t st) {
+  switch (a.D) {
+    case 64: return a.causal ? launch_one<T, 64, true, false, false, true>(a, st, n_wg)
+                             : launch_one<T, 64, false, false, false, true>(a, st, n_wg);
+    case 128: return a.causal ? launch_one<T, 128, true, false, false, true>(a, st, n_wg)
+                              : launch_one<T, 128, false, false, false, true>(a, st, n_wg);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_fwd_persistent(const FwdArgs& a, int n_wg, hipStream_t st) {
+  if (a.n_split != 1 || n_wg < 1) return hipErrorInvalidValue;
+  if (a.dtype == 2) return launch_persistent_t<__bf16>(a, n_wg, st);
+  return launch_persistent_t<_Float16>(a, n_wg, st);
 }
 
 hipError_t launch_fwd_mfma(const FwdArgs& a, hipStream_t st) {

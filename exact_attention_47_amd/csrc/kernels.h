@@ -54,6 +54,10 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t st);
 // packed (variable-length) batches on the bf16 / fp16 kernel, D = 64 / 128
 hipError_t launch_fwd_varlen(const FwdArgs& a, hipStream_t st);
 
+// the bf16 / fp16 kernel on a persistent grid of n_wg workgroups (unsplit,
+// D = 64 / 128); n_wg at most the CU count keeps every workgroup resident
+hipError_t launch_fwd_persistent(const FwdArgs& a, int n_wg, hipStream_t st);
+
 // short causal key ranges, D = 64 / 128 (two co-resident 4-wave workgroups per CU)
 hipError_t launch_fwd_short(const FwdArgs& a, hipStream_t st);
 int short_rows_per_block();

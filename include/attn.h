@@ -100,6 +100,31 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse
                 void* stream);
 
 /*
+ * attn_fwd_persistent -- attn_fwd on a persistent grid: a fixed number of
+ * workgroups, each resident on its own CU for the whole call, loops over the
+ * (b, h, query tile) items dealt to it ([GN] "Weitere Optimierungen und
+ * kuenftige Integration" lists the persistent kernel among the full paper's
+ * optimizations). Same operands, layout, masking, outputs and errors as
+ * attn_fwd, and the same bits as attn_fwd where attn_fwd runs the unsplit
+ * main kernel (long key ranges); the key range is never split.
+ *
+ *   dtype           ATTN_F16 or ATTN_BF16 (others: ATTN_ERR_UNSUPPORTED)
+ *   D               64 or 128 (others: ATTN_ERR_UNSUPPORTED)
+ *   num_workgroups  0 = one per CU of the current device; 1 .. CU count =
+ *                   that many (uses only that many CUs, leaving the others to
+ *                   concurrent work); more than the CU count or negative:
+ *                   ATTN_ERR_INVALID_ARG
+ *
+ * Items are dealt heaviest query tile first in a snake order (even rounds
+ * forward, odd rounds backward), which pairs heavy and light causal tiles so
+ * the workgroups finish together; the deal is fixed, so the results do not
+ * depend on timing. No workspace.
+ */
+int attn_fwd_persistent(const void* q, const void* k, const void* v, void* o, float* lse,
+                        int B, int H, int S_q, int S_k, int D, int causal, float scale,
+                        int dtype, int num_workgroups, void* stream);
+
+/*
  * attn_fwd_varlen -- attn_fwd over a packed batch of sequences of different
  * lengths ([GN] "Weitere Optimierungen und kuenftige Integration" lists
  * variable-length sequences among the full paper's optimizations; each

@@ -156,3 +156,26 @@ def rope(**kw):
 def test_rope_hadamard_quant_validation_rejects(kw, code):
     """Host-side checks of rope_hadamard_quant: each bad argument is refused before anything is enqueued."""
     assert rope(**kw) == code
+
+
+def persistent(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=1, H=2, S_q=128, S_k=128, D=128, causal=0, scale=0.125, dtype=2, n_wg=0)
+    a.update(kw)
+    return attn.load().attn_fwd_persistent(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["S_q"],
+                                           a["S_k"], a["D"], a["causal"], ctypes.c_float(a["scale"]), a["dtype"],
+                                           a["n_wg"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(n_wg=-1), attn.ERR_INVALID_ARG),
+    (dict(lse=None), attn.ERR_INVALID_ARG),
+    (dict(S_k=0), attn.ERR_INVALID_ARG),
+    (dict(causal=2), attn.ERR_INVALID_ARG),
+    (dict(dtype=0), attn.ERR_UNSUPPORTED),
+    (dict(D=256), attn.ERR_UNSUPPORTED),
+    (dict(causal=1, S_q=200, S_k=100), attn.ERR_UNSUPPORTED),
+    (dict(v=P + 8), attn.ERR_MISALIGNED),
+])
+def test_persistent_validation_rejects(kw, code):
+    """Host-side checks of attn_fwd_persistent: each bad argument is refused before the device is queried."""
+    assert persistent(**kw) == code

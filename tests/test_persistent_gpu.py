@@ -1,0 +1,103 @@
+"""GPU parity of attn_fwd_persistent (fixed grid, snake-dealt work) through the C ABI.
+
+Same bar as the dense path for bfloat16/float16 with N(0,1) inputs: O max-abs
+<= 1e-2, RMSE <= 2e-3, LSE max-abs <= 1e-3 against the oracle. The persistent
+grid runs the main kernel's per-tile code, so where attn_fwd also runs the
+unsplit main kernel (long key ranges) the two must agree bit for bit, whatever
+the number of workgroups.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from exact_attention_47_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+BF_MAX, BF_RMSE, LSE_MAX = 1e-2, 2e-3, 1e-3
+
+
+def note(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+def assert_close(o, lse, ro, rl, what):
+    d = np.abs(o.float().cpu().numpy().astype(np.float64) - ro)
+    mx, rm = float(d.max()), float(np.sqrt(np.mean(d ** 2)))
+    ls = float(np.abs(lse.cpu().numpy().astype(np.float64) - rl).max())
+    print(f"    {what}: O max {mx:.3e} rmse {rm:.3e} LSE max {ls:.3e}", flush=True)
+    assert mx <= BF_MAX and rm <= BF_RMSE and ls <= LSE_MAX, (what, mx, rm, ls)
+
+
+# (B, H, S_q, S_k, causal): several 256-row query tiles with ragged tails, S_q != S_k,
+# B*H both a multiple of 8 (per-XCD deal) and not
+CASES = [
+    (1, 3, 700, 700, True),
+    (1, 3, 700, 700, False),
+    (2, 4, 513, 1100, True),
+    (2, 4, 300, 900, False),
+    (1, 8, 1000, 1000, True),
+]
+
+
+@pytest.mark.parametrize("n_wg", [1, 3, 8, 0])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("case", range(len(CASES)))
+def test_persistent_against_oracle(gpu_lib, case, dtype, D, n_wg):
+    B, H, S_q, S_k, causal = CASES[case]
+    note(f"persistent B{B} H{H} S_q{S_q} S_k{S_k} causal={causal} {dtype} D{D} n_wg={n_wg}")
+    scale = D ** -0.5
+    q, k, v = inputs.qkv(B, H, S_q, S_k, D, seed=21 + case, dtype=dtype)
+    o, lse = gpu_lib.fwd_persistent(q.cuda(), k.cuda(), v.cuda(), causal=causal, scale=scale, num_workgroups=n_wg)
+    torch.cuda.synchronize()
+    ro, rl = oracle.attention(q.float().numpy(), k.float().numpy(), v.float().numpy(), causal, scale)
+    assert_close(o, lse, ro, rl, f"case {case}")
+
+
+@pytest.mark.parametrize("B,H,S,D,causal,n_wg", [
+    (2, 16, 8192, 128, True, 0),      # the causal 8K workload on one workgroup per CU
+    (2, 16, 8192, 128, True, 64),     # a quarter of the CUs
+    (2, 16, 8192, 128, False, 0),
+    (1, 5, 3000, 128, True, 0),       # B*H not a multiple of 8
+    (2, 32, 8192, 64, True, 0),
+    (1, 3, 5000, 64, False, 7),
+])
+def test_persistent_bitwise_equal_dense(gpu_lib, B, H, S, D, causal, n_wg):
+    note(f"persistent vs dense B{B} H{H} S{S} D{D} causal={causal} n_wg={n_wg}")
+    q, k, v = inputs.qkv(B, H, S, S, D, seed=4, dtype=torch.bfloat16, device="cuda")
+    o_d, l_d = gpu_lib.fwd(q, k, v, causal=causal)
+    o_p, l_p = gpu_lib.fwd_persistent(q, k, v, causal=causal, num_workgroups=n_wg)
+    torch.cuda.synchronize()
+    assert torch.equal(o_p, o_d) and torch.equal(l_p, l_d)
+
+
+def test_persistent_fullsize_sampled_rows(gpu_lib):
+    """Causal B2 H16 S8K D128 as the bench times it (one workgroup per CU): sampled rows of two heads."""
+    note("persistent full size causal B2 H16 S8192 D128")
+    B, H, S, D = 2, 16, 8192, 128
+    scale = 1 / math.sqrt(D)
+    q, k, v = inputs.qkv(B, H, S, S, D, seed=0, dtype=torch.bfloat16, device="cuda")
+    o, lse = gpu_lib.fwd_persistent(q, k, v, causal=True, scale=scale)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(3)
+    for b, h in [(0, 0), (1, 15)]:
+        rows = np.array(sorted({0, 1, S // 2, S - 1} | set(rng.integers(0, S, size=24).tolist())))
+        idx = torch.from_numpy(rows).cuda()
+        ro, rl = oracle.attention_rows(q[b, h, idx].float().cpu().numpy(), k[b, h].float().cpu().numpy(),
+                                       v[b, h].float().cpu().numpy(), rows, True, scale, s_q=S)
+        assert_close(o[b, h, idx], lse[b, h, idx], ro, rl, f"b{b} h{h}")
+
+
+def test_persistent_rejects_more_workgroups_than_cus(gpu_lib):
+    q, k, v = inputs.qkv(1, 2, 256, 256, 128, seed=1, dtype=torch.bfloat16, device="cuda")
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    with pytest.raises(gpu_lib.AttnError):
+        gpu_lib.fwd_persistent(q, k, v, num_workgroups=n_cu + 1)
+    o, _ = gpu_lib.fwd_persistent(q, k, v, num_workgroups=n_cu)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o.float()).all()
