@@ -70,6 +70,23 @@ bool use_short_kernel(int D, int causal, int S_k, int n_split) {
   return false;
 }
 
+// Causal D = 128 on the main kernel runs on the persistent grid: its snake
+// deal measured +0.8 to +2 % over the hardware-dealt grid from 4K to 16K
+// keys; D = 64 (-1 %) and non-causal work (+0.5 %) keep the plain grid.
+bool use_persistent(int D, int causal, int n_split) { return causal && D == 128 && n_split == 1; }
+
+// Compute units of the current device, asked once per device.
+int cu_count() {
+  static int cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  int n = dev < 64 ? cache[dev] : 0;
+  if (n > 0) return n;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return 0;
+  if (dev < 64) cache[dev] = n;
+  return n;
+}
+
 size_t ws_bytes(const Plan& p, int B, int H, int S_q, int D) {
   if (p.n_split <= 1) return 0;
   const size_t rows = (size_t)p.n_split * B * H * S_q;
@@ -123,9 +140,11 @@ int run_fwd(const void* q, const void* k, const void* v, void* o, float* lse, in
     a.lpart = (float*)((char*)buf + round_up(rows * D * sizeof(float), 256));
   }
   hipError_t e;
+  int n_cu = 0;
   if (dtype == ATTN_F32) e = attn::launch_fwd_f32(a, st);
   else if (p.n_split > 1 && S_q <= attn::decode_max_rows()) e = attn::launch_fwd_decode(a, st);
   else if (use_short_kernel(D, causal, S_k, p.n_split)) e = attn::launch_fwd_short(a, st);
+  else if (use_persistent(D, causal, p.n_split) && (n_cu = cu_count()) > 0) e = attn::launch_fwd_persistent(a, n_cu, st);
   else e = attn::launch_fwd_mfma(a, st);
   if (e == hipSuccess && p.n_split > 1) e = attn::launch_combine(a, st);
   if (need > 0 && own_ws) {
@@ -199,12 +218,7 @@ int attn_fwd_persistent(const void* q, const void* k, const void* v, void* o, fl
   if (rc == ATTN_OK && num_workgroups < 0) rc = ATTN_ERR_INVALID_ARG;
   if (rc == ATTN_OK && (dtype == ATTN_F32 || (D != 64 && D != 128))) rc = ATTN_ERR_UNSUPPORTED;
   int n_cu = 0;
-  if (rc == ATTN_OK) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n_cu <= 0)
-      rc = ATTN_ERR_LAUNCH;
-  }
+  if (rc == ATTN_OK && (n_cu = cu_count()) <= 0) rc = ATTN_ERR_LAUNCH;
   // one workgroup per CU at most: the kernel's workgroup fills a CU, so a
   // larger grid would no longer be resident at once
   if (rc == ATTN_OK && num_workgroups > n_cu) rc = ATTN_ERR_INVALID_ARG;
