@@ -15,6 +15,8 @@ typedef __bf16 v8bf16 __attribute__((ext_vector_type(8)));
 typedef _Float16 v8f16 __attribute__((ext_vector_type(8)));
 typedef __bf16 v4bf16 __attribute__((ext_vector_type(4)));
 typedef _Float16 v4f16 __attribute__((ext_vector_type(4)));
+typedef __bf16 v2bf16 __attribute__((ext_vector_type(2)));
+typedef _Float16 v2f16 __attribute__((ext_vector_type(2)));
 typedef int v2i __attribute__((ext_vector_type(2)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 

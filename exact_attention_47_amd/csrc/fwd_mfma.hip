@@ -35,9 +35,11 @@
 //   given the matching choice of keys for V^T).
 //
 // * Softmax in base 2 with the scale folded in: p = 2^(s * c - m), c =
-//   scale * log2(e). The reference m moves only when a row's maximum exceeds
-//   it by more than TAU (p <= 2^TAU): rescales of O become rare, and the
-//   result is still exact because the final O / l and LSE use the same m.
+//   scale * log2(e). The reference m moves only when a lane's sum of P over
+//   a tile exceeds 2^8 (which bounds every P by 2^8): the row maximum is
+//   then computed and P recomputed, so most tiles need neither the maximum
+//   nor a rescale of O, and the result is still exact because the final
+//   O / l and LSE use the same m.
 //
 // * LDS layout. Tiles are stored unpadded ([BN][D]) with a 16-byte-chunk XOR
 //   swizzle that depends on the row, so that the K reads (16 lanes per LDS
@@ -88,7 +90,7 @@ struct FwdCfg {
 template <int D> __device__ __forceinline__ int k_swz(int r) { return D == 64 ? (r >> 1) & 7 : r & 15; }
 template <int D> __device__ __forceinline__ int v_swz(int r) { return D == 64 ? 4 * ((r >> 1) & 1) : 4 * (r & 3); }
 
-constexpr float kTau = 8.0f;   // lazy-rescale threshold, log2 domain
+constexpr float kSumMax = 256.0f;   // lazy rescale: a lane's tile sum of P may reach 2^8
 constexpr int kVmcnt0 = 0x0070 | 0x0F00;   // s_waitcnt vmcnt(0), other counters unconstrained
 
 template <typename T, int D, int BN, bool CAUSAL, bool SPLIT, bool VARLEN, bool PERSIST>
@@ -380,38 +382,51 @@ fwd_mfma_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
             if (!ok) s[kb][4 * i + j] = kNegInf;
           }
     }
-    float x = kNegInf;
+    // P = 2^(s*c - m) with the row's current reference m, summed in float32
+    // and converted to the matrix operand type.
+    auto exps = [&]() {
+      const float ref = m == kNegInf ? 0.0f : m;
+      float ls = 0.0f;
 #pragma unroll
-    for (int kb = 0; kb < C::KB; kb++)
+      for (int kb = 0; kb < C::KB; kb++)
 #pragma unroll
-      for (int e = 0; e < 16; e++) x = fmaxf(x, s[kb][e]);
-    x = pair_max(x) * c;
-    if (__any(x > m + kTau)) {
+        for (int ks = 0; ks < 2; ks++) {
+          v8f pv;
+#pragma unroll
+          for (int e = 0; e < 8; e++) {
+            pv[e] = fast_exp2(__builtin_fmaf(s[kb][8 * ks + e], c, -ref));
+            ls += pv[e];
+          }
+          pf[kb][ks] = M::cvt(pv);
+        }
+      return ls;
+    };
+    // The reference only has to keep every P <= 2^8. A lane's tile sum
+    // bounds each of its P, so the row maximum is computed only when some
+    // sum exceeds 2^8 (or a row has no reference yet): then m moves to
+    // the maximum, O and l are rescaled, and P is recomputed. Any reference
+    // reached this way gives the exact result, as the final O / l and LSE
+    // use the same m.
+    float ls = __builtin_inff();                 // forces the slow path below
+    if (!__any(m == kNegInf)) ls = exps();
+    if (__any(!(ls <= kSumMax))) {
+      float x = kNegInf;
+#pragma unroll
+      for (int kb = 0; kb < C::KB; kb++)
+#pragma unroll
+        for (int e = 0; e < 16; e++) x = fmaxf(x, s[kb][e]);
+      x = pair_max(x) * c;
       const float mnew = fmaxf(m, x);
       const float ref = mnew == kNegInf ? 0.0f : mnew;
-      const float alpha = fast_exp2(m - ref);   // 0 when m was -inf
+      const float alpha = fast_exp2(m - ref);   // 0 when m was -inf, 1 when m stays
       m = mnew;
       l *= alpha;
 #pragma unroll
       for (int db = 0; db < C::DB; db++)
 #pragma unroll
         for (int e = 0; e < 16; e++) o[db][e] *= alpha;
+      ls = exps();
     }
-    const float ref = m == kNegInf ? 0.0f : m;
-    float ls = 0.0f;
-#pragma unroll
-    for (int kb = 0; kb < C::KB; kb++)
-#pragma unroll
-      for (int ks = 0; ks < 2; ks++) {
-        v8f pv;
-#pragma unroll
-        for (int e = 0; e < 8; e++) {
-          const float p = fast_exp2(__builtin_fmaf(s[kb][8 * ks + e], c, -ref));
-          pv[e] = p;
-          ls += p;
-        }
-        pf[kb][ks] = M::cvt(pv);
-      }
     l += ls;
   };
 
