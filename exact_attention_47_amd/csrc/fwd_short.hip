@@ -78,7 +78,7 @@ struct ShortCfg {
 template <int D> __device__ __forceinline__ int k_swz(int r) { return D == 64 ? (r >> 1) & 7 : r & 15; }
 template <int D> __device__ __forceinline__ int v_swz(int r) { return D == 64 ? 4 * ((r >> 1) & 1) : 4 * (r & 3); }
 
-constexpr float kTau = 8.0f;   // lazy-rescale threshold, log2 domain
+constexpr float kSumMax = 256.0f;   // lazy rescale: a lane's tile sum of P may reach 2^8
 
 template <int N> struct IC { static constexpr int value = N; };
 
@@ -249,38 +249,67 @@ fwd_short_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __re
             if (!ok) s[kb][4 * i + jx] = kNegInf;
           }
     }
-    float x = kNegInf;
+    // P = 2^(s*c - m) with the row's current reference m. The reference only
+    // has to keep every P <= 2^8.
+    frag pf[C::KB][2];
+    auto exps = [&](float& acc) {
+      const float ref = m == kNegInf ? 0.0f : m;
 #pragma unroll
-    for (int kb = 0; kb < C::KB; kb++)
+      for (int kb = 0; kb < C::KB; kb++)
 #pragma unroll
-      for (int e = 0; e < 16; e++) x = fmaxf(x, s[kb][e]);
-    x = pair_max(x) * c;
-    if (__any(x > m + kTau)) {
+        for (int ks = 0; ks < 2; ks++) {
+          v8f pv;
+#pragma unroll
+          for (int e = 0; e < 8; e++) {
+            pv[e] = fast_exp2(__builtin_fmaf(s[kb][8 * ks + e], c, -ref));
+            acc += pv[e];
+          }
+          pf[kb][ks] = M::cvt(pv);
+        }
+    };
+    auto move_reference = [&](float x) {     // m -> max(m, x), O and l rescaled
       const float mnew = fmaxf(m, x);
       const float r = mnew == kNegInf ? 0.0f : mnew;
-      const float alpha = fast_exp2(m - r);      // 0 when m was -inf
+      const float alpha = fast_exp2(m - r);      // 0 when m was -inf, 1 when m stays
       m = mnew;
       l *= alpha;
 #pragma unroll
       for (int db = 0; db < C::DB; db++)
 #pragma unroll
         for (int e = 0; e < 16; e++) o[db][e] *= alpha;
-    }
-    const float ref = m == kNegInf ? 0.0f : m;
-    frag pf[C::KB][2];
+    };
+    auto row_max = [&]() {
+      float x = kNegInf;
 #pragma unroll
-    for (int kb = 0; kb < C::KB; kb++)
+      for (int kb = 0; kb < C::KB; kb++)
 #pragma unroll
-      for (int ks = 0; ks < 2; ks++) {
-        v8f pv;
-#pragma unroll
-        for (int e = 0; e < 8; e++) {
-          const float p = fast_exp2(__builtin_fmaf(s[kb][8 * ks + e], c, -ref));
-          pv[e] = p;
-          l += p;
-        }
-        pf[kb][ks] = M::cvt(pv);
+        for (int e = 0; e < 16; e++) x = fmaxf(x, s[kb][e]);
+      return pair_max(x) * c;
+    };
+    if constexpr (D == 64) {
+      // A lane's tile sum bounds each of its P, so the row maximum is
+      // computed only when some sum exceeds 2^8 (or a row has no reference
+      // yet): then m moves to the maximum and P is recomputed. The final
+      // O / l and LSE use the same m, so any reference reached this way
+      // gives the exact result. (At D = 128 the extra code costs the
+      // three-wave register budget more than the skipped maximum saves.)
+      float ls = __builtin_inff();               // forces the slow path below
+      if (!__any(m == kNegInf)) {
+        ls = 0.0f;
+        exps(ls);
       }
+      if (__any(!(ls <= kSumMax))) {
+        move_reference(row_max());
+        ls = 0.0f;
+        exps(ls);
+      }
+      l += ls;
+    } else {
+      // the reference moves when a row's maximum exceeds it by more than 8
+      const float x = row_max();
+      if (__any(x > m + 8.0f)) move_reference(x);
+      exps(l);
+    }
     {
       constexpr int NP = C::KB * 2 * C::DB;
       const char* vl = rbuf + C::TILE;
