@@ -111,6 +111,8 @@ __global__ void __launch_bounds__(256) bwd_dot_kernel(const T* __restrict__ O, c
   if (row < rows && part == 0) Dd[row] = acc;
 }
 
+template <bool B> struct BIC { static constexpr bool value = B; };
+
 template <typename T, int D, int MODE, bool CAUSAL>
 __global__ void __launch_bounds__(256)
 __attribute__((amdgpu_waves_per_eu(MODE == 2 ? 3 : 2, MODE == 2 ? 3 : 2)))
@@ -271,40 +273,50 @@ bwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict
       }
     }
     // probabilities (and dS), masked where the key is outside the range or
-    // after the causal limit
+    // after the causal limit. The mask is evaluated only on tiles that hold
+    // such a pair for this wave's 32 outer rows (range tails, the causal
+    // diagonal); elsewhere every pair is allowed.
     const int orow = wr0 + nn;
+    const int t0 = t * C::BI;
+    const bool full = DQ ? (wr0 + 32 <= S_q && t0 + C::BI <= S_k && (!CAUSAL || t0 + C::BI - 1 <= wr0 + diag))
+                         : (t0 + C::BI <= S_q && wr0 + 32 <= S_k && (!CAUSAL || wr0 + 31 <= t0 + diag));
     float gv[16];
+    auto probs = [&](auto masked) {
+      constexpr bool MASKED = decltype(masked)::value;
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-      float l4[4], d4[4];
-      const int ir0 = t * C::BI + 8 * i + 4 * hh;   // inner rows ir0 .. ir0+3
-      if (!DQ) {
-        const float4 lv = *(const float4*)(st + 2 * C::TILE + (8 * i + 4 * hh) * 4);
-        l4[0] = lv.x * kLog2e; l4[1] = lv.y * kLog2e; l4[2] = lv.z * kLog2e; l4[3] = lv.w * kLog2e;
-        if (MODE == kDK) {
-          const float4 dv4 = *(const float4*)(st + 2 * C::TILE + 256 + (8 * i + 4 * hh) * 4);
-          d4[0] = dv4.x; d4[1] = dv4.y; d4[2] = dv4.z; d4[3] = dv4.w;
-        } else {
-          d4[0] = d4[1] = d4[2] = d4[3] = 0.0f;
+      for (int i = 0; i < 4; i++) {
+        float l4[4], d4[4];
+        const int ir0 = t0 + 8 * i + 4 * hh;          // inner rows ir0 .. ir0+3
+        if (!DQ) {
+          const float4 lv = *(const float4*)(st + 2 * C::TILE + (8 * i + 4 * hh) * 4);
+          l4[0] = lv.x * kLog2e; l4[1] = lv.y * kLog2e; l4[2] = lv.z * kLog2e; l4[3] = lv.w * kLog2e;
+          if (MODE == kDK) {
+            const float4 dv4 = *(const float4*)(st + 2 * C::TILE + 256 + (8 * i + 4 * hh) * 4);
+            d4[0] = dv4.x; d4[1] = dv4.y; d4[2] = dv4.z; d4[3] = dv4.w;
+          } else {
+            d4[0] = d4[1] = d4[2] = d4[3] = 0.0f;
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+          const int e = 4 * i + j;
+          const int ir = ir0 + j;
+          const int query = DQ ? orow : ir;
+          const int key = DQ ? ir : orow;
+          const bool ok = !MASKED || (query < S_q && key < S_k && (!CAUSAL || key <= query + diag));
+          const float l2 = DQ ? lse2_o : l4[j];
+          const float p = ok ? fast_exp2(__builtin_fmaf(s[e], c, -l2)) : 0.0f;
+          if (MODE == kDV) {
+            gv[e] = p;
+          } else {
+            const float ddv = DQ ? dd_o : d4[j];
+            gv[e] = p * (dp[e] - ddv);
+          }
         }
       }
-#pragma unroll
-      for (int j = 0; j < 4; j++) {
-        const int e = 4 * i + j;
-        const int ir = ir0 + j;
-        const int query = DQ ? orow : ir;
-        const int key = DQ ? ir : orow;
-        const bool ok = query < S_q && key < S_k && (!CAUSAL || key <= query + diag);
-        const float l2 = DQ ? lse2_o : l4[j];
-        const float p = ok ? fast_exp2(__builtin_fmaf(s[e], c, -l2)) : 0.0f;
-        if (MODE == kDV) {
-          gv[e] = p;
-        } else {
-          const float ddv = DQ ? dd_o : d4[j];
-          gv[e] = p * (dp[e] - ddv);
-        }
-      }
-    }
+    };
+    if (full) probs(BIC<false>());
+    else probs(BIC<true>());
     frag gf[2];
 #pragma unroll
     for (int ks = 0; ks < 2; ks++) {
