@@ -309,9 +309,10 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
   }
   hipStream_t st = (hipStream_t)stream;
   void* dd = nullptr;
-  if (hipMallocAsync(&dd, (size_t)B * H * S_q * sizeof(float), st) != hipSuccess) return ATTN_ERR_LAUNCH;
+  const size_t rows = (size_t)B * H * S_q;
+  if (hipMallocAsync(&dd, 2 * rows * sizeof(float), st) != hipSuccess) return ATTN_ERR_LAUNCH;
   attn::BwdArgs a;
-  a.q = q; a.k = k; a.v = v; a.o = o; a.dout = dout; a.lse = lse; a.dd = (float*)dd;
+  a.q = q; a.k = k; a.v = v; a.o = o; a.dout = dout; a.lse = lse; a.dd = (float*)dd; a.nl2 = (float*)dd + rows;
   a.dq = dq; a.dk = dk; a.dv = dv;
   a.B = B; a.H = H; a.S_q = S_q; a.S_k = S_k; a.D = D; a.causal = causal; a.dtype = dtype; a.scale = scale;
   hipError_t e = attn::launch_bwd(a, st);

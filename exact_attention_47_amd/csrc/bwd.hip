@@ -29,7 +29,10 @@
 // exactly as the forward pass reads V^T. Staged tiles use an XOR swizzle that
 // suits both read patterns (see bswz).
 //
-// Dd comes from a small first kernel (one row per D/8 lanes, float32 sum).
+// A small first kernel (one row per D/8 lanes, float32 sum) writes -Dd and
+// -log2(e) LSE per query row, the forms the tiles consume: P = exp2(S c +
+// (-log2(e) LSE)) is one multiply-add and an exp2, and dK's dP product starts
+// its accumulator at -Dd, so that dS = P * dP is one multiply.
 #include "common.h"
 #include "kernels.h"
 
@@ -65,7 +68,7 @@ struct BwdCfg {
   static constexpr int DB = D / 32;             // 32-wide blocks of D
   static constexpr int RB = 2 * D;              // bytes per row
   static constexpr int TILE = BI * RB;
-  static constexpr int STAGE = 2 * TILE + 512;  // X, Y, then 64 LSE and 64 Dd values (inner = queries)
+  static constexpr int STAGE = 2 * TILE + 512;  // X, Y, then 64 -log2(e) LSE and 64 -Dd values (inner = queries)
   static constexpr int NI = TILE / (NT * 16);   // direct loads per thread per tile
   static constexpr int RPI = 1024 / RB;         // rows per 1 KiB wave load
   static_assert(TILE % (NT * 16) == 0, "tile must split into 1 KiB wave loads");
@@ -89,10 +92,12 @@ __device__ __forceinline__ void load8f(const T* p, float* out) {
   for (int i = 0; i < 8; i++) out[i] = (float)e[i];
 }
 
-// Dd[row] = sum_d dO[row][d] * O[row][d], float32, D/8 lanes per row
+// nDd[row] = -sum_d dO[row][d] * O[row][d] (float32, D/8 lanes per row) and
+// nl2[row] = -log2(e) * LSE[row]
 template <typename T, int D>
 __global__ void __launch_bounds__(256) bwd_dot_kernel(const T* __restrict__ O, const T* __restrict__ dO,
-                                                       float* __restrict__ Dd, long rows)
+                                                       const float* __restrict__ LSE, float* __restrict__ nDd,
+                                                       float* __restrict__ nl2, long rows)
 {
   constexpr int LPR = D / 8;
   const long g = (long)blockIdx.x * 256 + threadIdx.x;
@@ -108,7 +113,10 @@ __global__ void __launch_bounds__(256) bwd_dot_kernel(const T* __restrict__ O, c
   }
 #pragma unroll
   for (int off = LPR / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
-  if (row < rows && part == 0) Dd[row] = acc;
+  if (row < rows && part == 0) {
+    nDd[row] = -acc;
+    nl2[row] = -(LSE[row] * kLog2e);
+  }
 }
 
 template <bool B> struct BIC { static constexpr bool value = B; };
@@ -117,7 +125,7 @@ template <typename T, int D, int MODE, bool CAUSAL>
 __global__ void __launch_bounds__(256)
 __attribute__((amdgpu_waves_per_eu(MODE == 2 ? 3 : 2, MODE == 2 ? 3 : 2)))
 bwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
-           const T* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dd,
+           const T* __restrict__ dO, const float* __restrict__ NL2, const float* __restrict__ NDd,
            T* __restrict__ Gout, int BH, int S_q, int S_k, int n_ot, float c, float gscale)
 {
   using C = BwdCfg<D>;
@@ -158,8 +166,8 @@ bwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict
   const T* O2 = DQ ? dO + qo : V + ko;          // outer, second product
   const T* Xg = DQ ? K + ko : Q + qo;           // inner, first product (and dQ / dK accumulation)
   const T* Yg = DQ ? V + ko : dO + qo;          // inner, second product (and dV accumulation)
-  const float* lseh = LSE + (size_t)bh * S_q;
-  const float* ddh = Dd + (size_t)bh * S_q;
+  const float* nl2h = NL2 + (size_t)bh * S_q;   // -log2(e) LSE
+  const float* nddh = NDd + (size_t)bh * S_q;   // -Dd
 
   // outer rows as B operands: lane (h, n) holds row wr0+n, d = 16 ds + 8 h .. +7
   frag of1[C::DS], of2[TWO ? C::DS : 1];
@@ -180,10 +188,10 @@ bwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict
     }
   }
   // per-lane scalars of the outer query row (mode dQ)
-  float lse2_o = 0.0f, dd_o = 0.0f;
+  float nl2_o = 0.0f, ndd_o = 0.0f;
   if (DQ && wr0 + nn < S_q) {
-    lse2_o = lseh[wr0 + nn] * kLog2e;
-    dd_o = ddh[wr0 + nn];
+    nl2_o = nl2h[wr0 + nn];
+    ndd_o = nddh[wr0 + nn];
   }
 
   // stage t: X rows 32t.., Y rows 32t.. (buffer loads; rows past the end read 0)
@@ -193,10 +201,10 @@ bwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict
   const int dma_u = ((lane * 16) % C::RB) / 16;
   // (offsets and destinations go through locals: a target builtin with
   // template-dependent argument expressions is dropped from the host pass)
-  // (inner = queries: wave 0 also stages the tile's LSE and Dd values, 64
-  // rows per instruction, rows past S_q read 0)
-  const __amdgpu_buffer_rsrc_t lrs = __builtin_amdgcn_make_buffer_rsrc((void*)lseh, (short)0, S_q * 4, 0x00020000);
-  const __amdgpu_buffer_rsrc_t drs = __builtin_amdgcn_make_buffer_rsrc((void*)ddh, (short)0, S_q * 4, 0x00020000);
+  // (inner = queries: wave 0 also stages the tile's -log2(e) LSE and -Dd
+  // values, 64 rows per instruction, rows past S_q read 0)
+  const __amdgpu_buffer_rsrc_t lrs = __builtin_amdgcn_make_buffer_rsrc((void*)nl2h, (short)0, S_q * 4, 0x00020000);
+  const __amdgpu_buffer_rsrc_t drs = __builtin_amdgcn_make_buffer_rsrc((void*)nddh, (short)0, S_q * 4, 0x00020000);
   auto issue_stage = [&](int t, char* base) {
     if (!DQ && wave == 0) {
       char* ld = base + 2 * C::TILE;
@@ -264,8 +272,18 @@ bwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict
     }
     v16f dp = {};
     if constexpr (TWO) {
+      if constexpr (DQ) {
 #pragma unroll
-      for (int e = 0; e < 16; e++) dp[e] = 0.0f;
+        for (int e = 0; e < 16; e++) dp[e] = 0.0f;
+      } else {
+        // dP - Dd in one product: the accumulator starts at the staged -Dd of
+        // the inner (query) row that each element belongs to
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          const float4 d4 = *(const float4*)(st + 2 * C::TILE + 256 + (8 * i + 4 * hh) * 4);
+          dp[4 * i + 0] = d4.x; dp[4 * i + 1] = d4.y; dp[4 * i + 2] = d4.z; dp[4 * i + 3] = d4.w;
+        }
+      }
 #pragma unroll
       for (int ds = 0; ds < C::DS; ds++) {
         const frag a = *(const frag*)(ys + k_rd[ds % NKR] + (ds / NKR) * 256);
@@ -285,17 +303,11 @@ bwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict
       constexpr bool MASKED = decltype(masked)::value;
 #pragma unroll
       for (int i = 0; i < 4; i++) {
-        float l4[4], d4[4];
+        float l4[4];
         const int ir0 = t0 + 8 * i + 4 * hh;          // inner rows ir0 .. ir0+3
         if (!DQ) {
           const float4 lv = *(const float4*)(st + 2 * C::TILE + (8 * i + 4 * hh) * 4);
-          l4[0] = lv.x * kLog2e; l4[1] = lv.y * kLog2e; l4[2] = lv.z * kLog2e; l4[3] = lv.w * kLog2e;
-          if (MODE == kDK) {
-            const float4 dv4 = *(const float4*)(st + 2 * C::TILE + 256 + (8 * i + 4 * hh) * 4);
-            d4[0] = dv4.x; d4[1] = dv4.y; d4[2] = dv4.z; d4[3] = dv4.w;
-          } else {
-            d4[0] = d4[1] = d4[2] = d4[3] = 0.0f;
-          }
+          l4[0] = lv.x; l4[1] = lv.y; l4[2] = lv.z; l4[3] = lv.w;
         }
 #pragma unroll
         for (int j = 0; j < 4; j++) {
@@ -304,14 +316,11 @@ bwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict
           const int query = DQ ? orow : ir;
           const int key = DQ ? ir : orow;
           const bool ok = !MASKED || (query < S_q && key < S_k && (!CAUSAL || key <= query + diag));
-          const float l2 = DQ ? lse2_o : l4[j];
-          const float p = ok ? fast_exp2(__builtin_fmaf(s[e], c, -l2)) : 0.0f;
-          if (MODE == kDV) {
-            gv[e] = p;
-          } else {
-            const float ddv = DQ ? dd_o : d4[j];
-            gv[e] = p * (dp[e] - ddv);
-          }
+          const float nl2 = DQ ? nl2_o : l4[j];
+          const float p = ok ? fast_exp2(__builtin_fmaf(s[e], c, nl2)) : 0.0f;
+          if (MODE == kDV) gv[e] = p;
+          else if (MODE == kDK) gv[e] = p * dp[e];   // dp already holds dP - Dd
+          else gv[e] = p * (dp[e] + ndd_o);
         }
       }
     };
@@ -392,11 +401,11 @@ hipError_t launch_mode(const BwdArgs& a, hipStream_t st) {
   const float gscale = MODE == kDV ? 1.0f : a.scale;
   if (a.causal)
     hipLaunchKernelGGL((bwd_kernel<T, D, MODE, true>), grid, dim3(C::NT), 0, st, (const T*)a.q, (const T*)a.k,
-                       (const T*)a.v, (const T*)a.dout, a.lse, a.dd, out, a.B * a.H, a.S_q, a.S_k, n_ot,
+                       (const T*)a.v, (const T*)a.dout, a.nl2, a.dd, out, a.B * a.H, a.S_q, a.S_k, n_ot,
                        a.scale * kLog2e, gscale);
   else
     hipLaunchKernelGGL((bwd_kernel<T, D, MODE, false>), grid, dim3(C::NT), 0, st, (const T*)a.q, (const T*)a.k,
-                       (const T*)a.v, (const T*)a.dout, a.lse, a.dd, out, a.B * a.H, a.S_q, a.S_k, n_ot,
+                       (const T*)a.v, (const T*)a.dout, a.nl2, a.dd, out, a.B * a.H, a.S_q, a.S_k, n_ot,
                        a.scale * kLog2e, gscale);
   return hipGetLastError();
 }
@@ -408,7 +417,7 @@ hipError_t launch_d(const BwdArgs& a, hipStream_t st) {
   const long rows = (long)a.B * a.H * a.S_q;
   const long threads = rows * (D / 8);
   hipLaunchKernelGGL((bwd_dot_kernel<T, D>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st,
-                     (const T*)a.o, (const T*)a.dout, a.dd, rows);
+                     (const T*)a.o, (const T*)a.dout, a.lse, a.dd, a.nl2, rows);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if ((e = launch_mode<T, D, kDQ>(a, st)) != hipSuccess) return e;

@@ -40,7 +40,8 @@ struct BwdArgs {
   const void* o;
   const void* dout;
   const float* lse;    // [B*H][S_q], natural log, from the forward pass
-  float* dd;           // workspace [B*H][S_q]: rowsum(dO * O)
+  float* dd;           // workspace [B*H][S_q]: -rowsum(dO * O)
+  float* nl2;          // workspace [B*H][S_q]: -log2(e) * LSE
   void* dq;
   void* dk;
   void* dv;
