@@ -142,10 +142,21 @@ bwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict
   const int hh = lane >> 5;
   const int nn = lane & 31;
 
-  const int work = xcd_swizzle(blockIdx.x, BH * n_ot);
-  int ot = work % n_ot;
-  const int bh = work / n_ot;
-  if (CAUSAL && DQ) ot = n_ot - 1 - ot;        // late query tiles have the most keys
+  int ot, bh;
+  if (!CAUSAL) {
+    const int work = xcd_swizzle(blockIdx.x, BH * n_ot);
+    ot = work % n_ot;
+    bh = work / n_ot;
+  } else {
+    // causal: outer blocks go out heaviest first over all (b, h) at a time
+    // (late query tiles for dQ, early key blocks for dK and dV), so that no
+    // XCD is left with a head's heavy blocks at the end; the hardware deals
+    // consecutive workgroups to the 8 XCDs in turn, so (b, h) stays on XCD
+    // bh % 8 when B*H is a multiple of 8
+    const int level = blockIdx.x / BH;
+    bh = blockIdx.x % BH;
+    ot = DQ ? n_ot - 1 - level : level;
+  }
   const int S_o = DQ ? S_q : S_k;
   const int S_i = DQ ? S_k : S_q;
   const int o0 = ot * C::BO;
