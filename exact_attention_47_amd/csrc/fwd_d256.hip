@@ -83,13 +83,22 @@ fwd_d256_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
   const int nn = lane & 31;        // query column owned by this lane
 
   // ---- which (b*h, q tile, split) this workgroup computes
-  const int n_work = BH * n_qt * n_split;
-  int work = xcd_swizzle(blockIdx.x, n_work);
-  const int split = work % n_split;
-  work /= n_split;
-  int qt = work % n_qt;
-  const int bh = work / n_qt;
-  if (CAUSAL) qt = n_qt - 1 - qt;  // heaviest query tiles first
+  int split = 0, qt, bh;
+  if (CAUSAL && !SPLIT && n_qt >= 16) {
+    // query tiles heaviest first over all (b, h) at a time; consecutive
+    // workgroups go to the 8 XCDs in turn, so (b, h) stays on XCD bh % 8
+    // when B*H is a multiple of 8
+    qt = n_qt - 1 - (int)(blockIdx.x / BH);
+    bh = blockIdx.x % BH;
+  } else {
+    const int n_work = BH * n_qt * n_split;
+    int work = xcd_swizzle(blockIdx.x, n_work);
+    split = work % n_split;
+    work /= n_split;
+    qt = work % n_qt;
+    bh = work / n_qt;
+    if (CAUSAL) qt = n_qt - 1 - qt;  // heaviest query tiles first
+  }
 
   const int q0 = qt * C::BM;
   const int wr0 = q0 + wave * C::RPW;          // first row of this wave
