@@ -111,10 +111,19 @@ fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ K8, c
   const int nn = lane & 31;
 
   const int n_work = BH * n_qt;
-  const int work = xcd_swizzle(blockIdx.x, n_work);
-  int qt = work % n_qt;
-  const int bh = work / n_qt;
-  if (CAUSAL) qt = n_qt - 1 - qt;       // heaviest query tiles first
+  int qt, bh;
+  if (CAUSAL && n_qt >= 16) {
+    // query tiles heaviest first over all (b, h) at a time; consecutive
+    // workgroups go to the 8 XCDs in turn, so (b, h) stays on XCD bh % 8
+    // when B*H is a multiple of 8
+    qt = n_qt - 1 - (int)(blockIdx.x / BH);
+    bh = blockIdx.x % BH;
+  } else {
+    const int work = xcd_swizzle(blockIdx.x, n_work);
+    qt = work % n_qt;
+    bh = work / n_qt;
+    if (CAUSAL) qt = n_qt - 1 - qt;     // heaviest query tiles first
+  }
   const int q0 = qt * BM8;
   const int wr0 = q0 + wave * 32;
   const int diag = S_k - S_q;
