@@ -204,6 +204,9 @@ bwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict
     nl2_o = nl2h[wr0 + nn];
     ndd_o = nddh[wr0 + nn];
   }
+  v16f dd_init;
+#pragma unroll
+  for (int e = 0; e < 16; e++) dd_init[e] = ndd_o;
 
   // stage t: X rows 32t.., Y rows 32t.. (buffer loads; rows past the end read 0)
   const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc((void*)Xg, (short)0, S_i * C::RB, 0x00020000);
@@ -284,8 +287,9 @@ bwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict
     v16f dp = {};
     if constexpr (TWO) {
       if constexpr (DQ) {
-#pragma unroll
-        for (int e = 0; e < 16; e++) dp[e] = 0.0f;
+        // every element of a lane belongs to its outer (query) row: the
+        // product starts from a register block that holds that row's -Dd
+        dp = dd_init;
       } else {
         // dP - Dd in one product: the accumulator starts at the staged -Dd of
         // the inner (query) row that each element belongs to
@@ -330,8 +334,7 @@ bwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict
           const float nl2 = DQ ? nl2_o : l4[j];
           const float p = ok ? fast_exp2(__builtin_fmaf(s[e], c, nl2)) : 0.0f;
           if (MODE == kDV) gv[e] = p;
-          else if (MODE == kDK) gv[e] = p * dp[e];   // dp already holds dP - Dd
-          else gv[e] = p * (dp[e] + ndd_o);
+          else gv[e] = p * dp[e];                    // dp already holds dP - Dd
         }
       }
     };
