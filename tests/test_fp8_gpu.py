@@ -109,7 +109,9 @@ def _pipeline(lib, q, k, v, sg, causal, scale):
 
 
 @pytest.mark.parametrize("S_q,S_k,causal", [(520, 520, False), (520, 520, True), (300, 700, True),
-                                            (70, 200, False), (1, 130, False)])
+                                            (70, 200, False), (1, 130, False),
+                                            # 16 or more query tiles: causal work dealt heaviest first over all heads
+                                            (2100, 2100, True), (2200, 2500, True)])
 def test_fp8_attention_against_dequantized_oracle(gpu_lib, S_q, S_k, causal):
     note(f"fp8 attention S_q{S_q} S_k{S_k} causal={causal}")
     B, H, D = 1, 2, 128
@@ -127,14 +129,19 @@ def test_fp8_attention_against_dequantized_oracle(gpu_lib, S_q, S_k, causal):
     sim_p, _ = oracle.fp8_attention_sim(q.float().numpy(), k.float().numpy(), v.float().numpy(), causal,
                                         scale, "hadamard", sg.numpy(), p_quant=True)
     p_err = oracle.rmse(sim_p, ref)
+    p_max = float(np.abs(sim_p - ref).max())
     rm = float(np.sqrt(np.mean(err ** 2)))
     lse_err = float(np.abs(lse.cpu().numpy() - ref_lse).max())
-    print(f"    fp8: O rmse {rm:.3e} (P-rounding sim {p_err:.3e}) max {err.max():.3e} LSE max {lse_err:.3e}")
+    print(f"    fp8: O rmse {rm:.3e} (P-rounding sim {p_err:.3e}) max {err.max():.3e} (sim {p_max:.3e}) "
+          f"LSE max {lse_err:.3e}")
     # P rounding relative to the running (not final) row maximum and bf16 output
     # rounding: the RMSE stays within 2x the simulated P-rounding error plus the
-    # bf16 rounding floor; LSE uses unrounded P, so only float32 error remains.
+    # bf16 rounding floor, and the largest error within 2x the simulated largest
+    # plus that floor (at least 0.1: a row that leans on an outlier value of V,
+    # |V| up to about 40, carries its P rounding times that value); LSE uses
+    # unrounded P, so only float32 error remains.
     assert rm <= 2.0 * p_err + 2e-3
-    assert float(err.max()) <= 0.1
+    assert float(err.max()) <= max(0.1, 2.0 * p_max + 2e-2)
     assert lse_err <= 1e-3
 
 
