@@ -199,6 +199,20 @@ def test_kernel_boundary_key_ranges(gpu_lib, D, causal, S_q, S_k):
     _fullsize(gpu_lib, 1, 4, S_q, S_k, D, causal)
 
 
+@pytest.mark.parametrize("dt,S_q,S_k", [(torch.bfloat16, 4100, 4100), (torch.float16, 4000, 4300)])
+def test_d256_causal_many_query_tiles(gpu_lib, dt, S_q, S_k):
+    """D = 256 causal with 16 or more 256-row query tiles (ragged), the range where the tiles are dealt
+    heaviest first over all heads; every element against the oracle."""
+    note(f"d256 causal {dt} S_q{S_q} S_k{S_k}")
+    B, H, D = 1, 1, 256
+    q, k, v = inputs.qkv(B, H, S_q, S_k, D, seed=12, dtype=dt)
+    scale = 1 / math.sqrt(D)
+    o, lse = gpu_lib.fwd(q.cuda(), k.cuda(), v.cuda(), causal=True, scale=scale)
+    torch.cuda.synchronize()
+    ro, rl = oracle.attention(q.float().numpy(), k.float().numpy(), v.float().numpy(), True, scale)
+    assert_bf(o, lse, ro, rl, "d256 causal")
+
+
 def test_fullsize_d256_causal_8k(gpu_lib):
     note("full causal D256 H8 S8192 B2")
     _fullsize(gpu_lib, 2, 8, 8192, 8192, 256, True)
