@@ -19,12 +19,13 @@
 //   mode dK: outer = keys, inner = query rows:  S = Q K^T,  dP = dO V^T,
 //            dK^T += Q^T dS
 //   mode dV: outer = keys, inner = query rows:  S = Q K^T,  dV^T += dO^T P
+//   mode dKV (D = 64): the dK and dV modes in one pass, S and P computed once
 //
 // Splitting dK and dV recomputes S once more (eight products per tile pair
 // instead of five) but keeps each wave under the 256 registers that two waves
 // per SIMD allow, and every gradient is a plain sum in a fixed order: results
-// are deterministic (no atomics). At D = 64 both accumulators fit, and a
-// fourth mode (dKV) computes dK and dV in one pass (seven products). The A operands of the accumulations (K^T,
+// are deterministic (no atomics). At D = 64 both accumulators fit, and the
+// dKV mode needs seven products. The A operands of the accumulations (K^T,
 // Q^T, dO^T) are read from the staged tiles with ds_read_b64_tr_b16, choosing
 // for each k slot the inner row that the probability fragment holds there,
 // exactly as the forward pass reads V^T. Staged tiles use an XOR swizzle that
