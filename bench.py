@@ -153,8 +153,8 @@ def varlen_point(causal=True, steps=10, warmup=3):
 
 
 def bwd_point(causal, B=2, H=16, S=8192, D=128, steps=10, warmup=3):
-    """Backward pass (dQ, dK, dV) at the headline shape; FLOPs counted as 2.5x the forward's
-    (the five products S, dP, dV, dQ, dK; the kernels recompute S twice more)."""
+    """Backward pass (dQ, dK, dV), by default at the headline shape; FLOPs counted as 2.5x the forward's
+    (the five products S, dP, dV, dQ, dK; the kernels recompute S twice more at D = 128, once at D = 64)."""
     q, k, v = inputs.qkv(B, H, S, S, D, seed=0, dtype=torch.bfloat16, device="cuda")
     do = inputs.normal((B, H, S, D), 0, inputs.TENSOR_OUTLIER, dtype=torch.bfloat16, device="cuda")
     scale = 1 / math.sqrt(D)
@@ -235,7 +235,7 @@ def main():
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["fp8", "decode", "d256", "causal_sweep", "d64_sweep", "varlen", "bwd",
-                                       "persistent"],
+                                       "bwd_d64", "persistent"],
                     default=None,
                     help="run just this extra workload and print its JSON (for profiling one kernel family)")
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -271,6 +271,7 @@ def main():
                                   for n in (512, 1024, 2048, 4096, 8192, 16384)],
             "varlen": lambda: [varlen_point(c, steps=st, warmup=wu) for c in (True, False)],
             "bwd": lambda: [bwd_point(c, steps=st, warmup=wu) for c in (False, True)],
+            "bwd_d64": lambda: [bwd_point(c, B=4, H=32, S=4096, D=64, steps=st, warmup=wu) for c in (False, True)],
             "persistent": lambda: persistent_points(steps=st, warmup=wu),
         }
         print(json.dumps({"only": args.only, "result": runs[args.only]()}), flush=True)
@@ -340,6 +341,9 @@ def main():
         extras["fp8_pipeline_8k"] = fp8_point()
         extras["varlen_16k_tokens"] = [varlen_point(True), varlen_point(False)]
         extras["backward_8k"] = [bwd_point(False), bwd_point(True)]
+        # D = 64 runs dK and dV in one pass (S and P once for both)
+        extras["backward_d64_4k"] = [bwd_point(False, B=4, H=32, S=4096, D=64),
+                                     bwd_point(True, B=4, H=32, S=4096, D=64)]
         extras["persistent_causal"] = persistent_points()
         out["extras"] = extras
     if not args.no_cpu_baseline:
