@@ -59,13 +59,14 @@ size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 // Short key ranges run on the short-range kernel (three or four small
 // workgroups per CU hide one another's start-up and memory waits), long ones
 // on the main kernel. Crossovers measured on the sweeps: D = 64 up to 4096
-// keys (+33 % at 512, +2 % at 4096, -1 % at 8192), D = 128 causal up to 2048
-// (+14 % at 512, -10 % at 4096), D = 128 non-causal up to 1024 (+16 % at 512,
-// -2 % at 2048). Requested splits always go to the main kernel, whose key
-// tile the split plan uses.
+// keys (+33 % at 512, +2 % at 4096, -1 to -2.6 % at 8192 and 16384), causal
+// D = 64 up to 8192 (+4.8 % at 8192; at 16384 +1 % with 32 heads, -7 % with
+// 8), D = 128 causal up to 2048 (+14 % at 512, equal at 4096, -6 % at 8192),
+// D = 128 non-causal up to 1024 (+16 % at 512, -2 % at 2048). Requested
+// splits always go to the main kernel, whose key tile the split plan uses.
 bool use_short_kernel(int D, int causal, int S_k, int n_split) {
   if (n_split != 1) return false;
-  if (D == 64) return S_k <= 4096;
+  if (D == 64) return S_k <= (causal ? 8192 : 4096);
   if (D == 128) return S_k <= (causal ? 2048 : 1024);
   return false;
 }

@@ -190,11 +190,12 @@ def test_fullsize_causal_d128_sweep(gpu_lib, S):
 
 @pytest.mark.parametrize("D,causal,S_q,S_k", [
     (64, False, 300, 4096), (64, False, 300, 4097), (64, True, 4096, 4096), (64, True, 1000, 4097),
+    (64, True, 8192, 8192), (64, True, 3000, 8193),
     (128, False, 777, 1024), (128, False, 777, 1025), (128, True, 2048, 2048), (128, True, 1500, 2049),
 ])
 def test_kernel_boundary_key_ranges(gpu_lib, D, causal, S_q, S_k):
     """Key-range lengths on both sides of the limit between the short-range and the main kernel
-    (D=64: 4096 keys; D=128: 1024 non-causal, 2048 causal), ragged and with S_q != S_k."""
+    (D=64: 4096 keys non-causal, 8192 causal; D=128: 1024 non-causal, 2048 causal), ragged and with S_q != S_k."""
     note(f"boundary D{D} causal={causal} S_q{S_q} S_k{S_k}")
     _fullsize(gpu_lib, 1, 4, S_q, S_k, D, causal)
 
