@@ -49,6 +49,9 @@ def run_case(lib, B, H, S_q, S_k, D, causal, dt, seed):
 CASES = [
     (1, 2, 200, 200, 64, False), (1, 2, 200, 200, 128, True), (1, 2, 100, 333, 128, False),
     (1, 2, 130, 257, 64, True), (2, 1, 1, 70, 128, False), (1, 1, 33, 33, 128, True),
+    # several 128-row outer blocks per head: interior (unmasked) tiles, the causal heaviest-first deal,
+    # and at D = 64 the fused dK/dV pass over many inner tiles
+    (1, 2, 1000, 1000, 64, True), (1, 2, 700, 1100, 64, False), (1, 2, 900, 900, 128, True),
 ]
 
 
