@@ -84,6 +84,19 @@ def test_hadamard_quant_fullsize_bitexact(gpu_lib):
     assert int((x8.cpu().numpy() != rc).sum()) == 0
 
 
+@pytest.mark.parametrize("shape", [(1, 5, 3001, 128), (2, 16, 8192, 128)], ids=["ragged", "fullsize"])
+def test_quant_per_tensor_bitexact_sizes(gpu_lib, shape):
+    """Sizes at which each thread of the maximum and code passes runs its eight-loads-in-flight loop
+    (the small case below only reaches the remainder loop); the full size is the FP8 workload's V."""
+    note(f"quant_per_tensor {shape}")
+    x = inputs.with_outliers(shape, 0, inputs.TENSOR_V, dtype=torch.bfloat16, device="cuda")
+    x8, sc = gpu_lib.quant_per_tensor(x)
+    torch.cuda.synchronize()
+    rc, rs = oracle.quantize_per_tensor(x.float().cpu().numpy())
+    assert sc.cpu().numpy().view(np.uint32)[0] == np.float32(rs).view(np.uint32)
+    np.testing.assert_array_equal(x8.cpu().numpy(), rc)
+
+
 @pytest.mark.parametrize("transposed", [False, True])
 def test_quant_per_tensor_bitexact(gpu_lib, transposed):
     note(f"quant_per_tensor transposed={transposed}")
