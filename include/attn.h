@@ -176,8 +176,9 @@ int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float*
  * ATTN_BF16 or ATTN_F16 and D is 64 or 128 (otherwise ATTN_ERR_UNSUPPORTED);
  * causal with S_q > S_k is ATTN_ERR_UNSUPPORTED as in attn_fwd. Accumulation
  * is float32 in a fixed order (deterministic); the gradients are rounded to
- * dtype. A float32 scratch of B*H*S_q values comes from the stream-ordered
- * allocator on `stream` and is released on it.
+ * dtype. A float32 scratch of 2*B*H*S_q values (per query row: -rowsum(dO * O)
+ * and -log2(e) LSE) comes from the stream-ordered allocator on `stream` and is
+ * released on it.
  */
 int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
              const void* dout, void* dq, void* dk, void* dv, int B, int H, int S_q, int S_k,
