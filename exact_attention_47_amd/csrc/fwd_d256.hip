@@ -19,7 +19,8 @@
 // V: chunk ^ 4 (row & 3)) so that the K reads (16 lanes per cycle over 16
 // rows) and the transposed V reads (32 lanes per cycle over 4 rows x 64
 // bytes) touch every bank of the 64-bank LDS once. Rows past the end of K/V
-// read zeros (their scores are masked).
+// read zeros (their scores are masked): the tile that reaches past the end
+// is loaded with range-checked offsets.
 #include "common.h"
 #include "kernels.h"
 
@@ -149,17 +150,35 @@ fwd_d256_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
   }
   // (offsets and destinations go through locals: a target builtin with
   // template-dependent argument expressions is dropped from the host pass)
+  // The buffer range check covers the per-lane offset and not the scalar
+  // one: a tile that reaches past the last row puts its whole offset in the
+  // per-lane part, so that its rows past the end read zeros.
   auto issue_tile = [&](int key0, char* base) {
+    if (key0 + C::BN <= S_k) {
 #pragma unroll
-    for (int i = 0; i < C::NI; i++) {
-      const int blk = i * C::NW + wave;
-      char* kdst = base + blk * 1024;
-      char* vdst = base + C::TILE + blk * 1024;
-      const int soff = key0 * C::RB + blk * 1024;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (__attribute__((address_space(3))) void*)kdst, 16, lane_k,
-                                               soff, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (__attribute__((address_space(3))) void*)vdst, 16, lane_v,
-                                               soff, 0, 0);
+      for (int i = 0; i < C::NI; i++) {
+        const int blk = i * C::NW + wave;
+        char* kdst = base + blk * 1024;
+        char* vdst = base + C::TILE + blk * 1024;
+        const int soff = key0 * C::RB + blk * 1024;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (__attribute__((address_space(3))) void*)kdst, 16, lane_k,
+                                                 soff, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (__attribute__((address_space(3))) void*)vdst, 16, lane_v,
+                                                 soff, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < C::NI; i++) {
+        const int blk = i * C::NW + wave;
+        char* kdst = base + blk * 1024;
+        char* vdst = base + C::TILE + blk * 1024;
+        const int koff = lane_k + key0 * C::RB + blk * 1024;
+        const int voff = lane_v + key0 * C::RB + blk * 1024;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (__attribute__((address_space(3))) void*)kdst, 16, koff,
+                                                 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (__attribute__((address_space(3))) void*)vdst, 16, voff,
+                                                 0, 0, 0);
+      }
     }
   };
 

@@ -157,7 +157,7 @@ fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ K8, c
   }
 
   // stage j = K(j), V(j): every wave issues NI8 K and NI8 V loads (1 KiB =
-  // 8 rows each) on per-head buffer resources; rows past the end read zeros
+  // 8 rows each) on per-head buffer resources
   const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)Kh, (short)0, S_k * D8, 0x00020000);
   const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)Vh, (short)0, S_k * D8, 0x00020000);
   int lane_k[NI8], lane_v[NI8];
@@ -169,15 +169,32 @@ fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ K8, c
   }
   // (offsets and destinations go through locals: a target builtin with
   // template-dependent argument expressions is dropped from the host pass)
+  // The buffer range check covers the per-lane offset and not the scalar
+  // one, so the tile offset rides in the scalar part only for tiles wholly
+  // inside K and V. The last tiles (partial, and the two fetched past the
+  // end so that every step issues the same loads and the wait counts stay
+  // exact) put their whole offset in the per-lane part: those rows read
+  // zeros and touch no memory outside the tensors.
   auto issue_stage = [&](int j, char* base) {
     const int soff = j * TILE8;
+    if ((j + 1) * BN8 <= S_k) {
 #pragma unroll
-    for (int i = 0; i < NI8; i++) {
-      char* kdst = base + (i * NW8 + wave) * 1024;
-      char* vdst = base + TILE8 + (i * NW8 + wave) * 1024;
-      const int lk = lane_k[i], lv = lane_v[i];
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (__attribute__((address_space(3))) void*)kdst, 16, lk, soff, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (__attribute__((address_space(3))) void*)vdst, 16, lv, soff, 0, 0);
+      for (int i = 0; i < NI8; i++) {
+        char* kdst = base + (i * NW8 + wave) * 1024;
+        char* vdst = base + TILE8 + (i * NW8 + wave) * 1024;
+        const int lk = lane_k[i], lv = lane_v[i];
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (__attribute__((address_space(3))) void*)kdst, 16, lk, soff, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (__attribute__((address_space(3))) void*)vdst, 16, lv, soff, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < NI8; i++) {
+        char* kdst = base + (i * NW8 + wave) * 1024;
+        char* vdst = base + TILE8 + (i * NW8 + wave) * 1024;
+        const int lk = lane_k[i] + soff, lv = lane_v[i] + soff;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (__attribute__((address_space(3))) void*)kdst, 16, lk, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (__attribute__((address_space(3))) void*)vdst, 16, lv, 0, 0, 0);
+      }
     }
   };
 

@@ -236,11 +236,15 @@ fwd_mfma_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
   // stage s = K(s) (if s < n_tiles) and V(s-1) (if s >= 1) into buffer s & 1.
   // Each wave instruction fills 1 KiB (RPI rows); lane i lands at byte 16*i
   // and fetches the logical chunk the swizzle stores there. The loads are
-  // buffer loads on per-head resources: rows past the end of K or V read
-  // zeros (their scores are masked). The rows a lane loads step by 16 (D=128)
-  // or 32 (D=64) between its instructions, which leaves both swizzles
+  // buffer loads on per-head resources. The rows a lane loads step by 16
+  // (D=128) or 32 (D=64) between its instructions, which leaves both swizzles
   // unchanged, so its part of the offset is one constant and the rest (tile
   // row and 1 KiB block) is wave-uniform: no vector arithmetic per load.
+  // The buffer range check covers the per-lane offset and not the scalar
+  // one, so that split serves only tiles that lie wholly inside K and V. A
+  // tile that reaches past the last row puts its whole offset in the
+  // per-lane part: the rows past the end then read zeros (their scores are
+  // masked, and zero V rows keep 0 * V finite whatever memory follows).
   // (packed rows are strided: the range ends after the last row's D elements)
   const int kv_bytes = VARLEN ? (S_k > 0 ? (S_k - 1) * RBg + C::RB : 0) : S_k * C::RB;
   const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)Kh, (short)0, kv_bytes, 0x00020000);
@@ -255,30 +259,31 @@ fwd_mfma_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
   }
   // (offsets and destinations go through locals: a target builtin with
   // template-dependent argument expressions is dropped from the host pass)
-  auto issue_stage = [&](int s) {
-    char* base = lds + (s & 1) * C::STAGE;
-    if (s < n_tiles) {
-      const int row0 = k_lo + s * C::BN;
+  auto load_tile = [&](__amdgpu_buffer_rsrc_t rs, int lane_off, int row0, char* tb) {
+    if (row0 + C::BN <= S_k) {
 #pragma unroll
       for (int i = 0; i < 2 * C::NI; i++) {
         const int blk = i * 4 + wave;                // 1 KiB block of the tile
-        char* dst = base + blk * 1024;
+        char* dst = tb + blk * 1024;
         const int soff = (row0 + blk * C::RPI) * RBg;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (__attribute__((address_space(3))) void*)dst, 16, lane_k,
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)dst, 16, lane_off,
                                                  soff, 0, 0);
       }
-    }
-    if (s >= 1 && s - 1 < n_tiles) {
-      const int row0 = k_lo + (s - 1) * C::BN;
+    } else {
 #pragma unroll
       for (int i = 0; i < 2 * C::NI; i++) {
         const int blk = i * 4 + wave;
-        char* dst = base + C::TILE + blk * 1024;
-        const int soff = (row0 + blk * C::RPI) * RBg;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (__attribute__((address_space(3))) void*)dst, 16, lane_v,
-                                                 soff, 0, 0);
+        char* dst = tb + blk * 1024;
+        const int voff = lane_off + (row0 + blk * C::RPI) * RBg;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)dst, 16, voff,
+                                                 0, 0, 0);
       }
     }
+  };
+  auto issue_stage = [&](int s) {
+    char* base = lds + (s & 1) * C::STAGE;
+    if (s < n_tiles) load_tile(krs, lane_k, k_lo + s * C::BN, base);
+    if (s >= 1 && s - 1 < n_tiles) load_tile(vrs, lane_v, k_lo + (s - 1) * C::BN, base + C::TILE);
   };
 
   // ---- per-lane LDS read offsets (swizzle folded in)
