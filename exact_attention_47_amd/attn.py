@@ -36,6 +36,7 @@ _SIGS = {
     "attn_status_string": (ctypes.c_char_p, [_i]),
     "attn_fwd": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i, _vp]),
     "attn_fwd_ex": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i, _i, _vp, _sz, _vp]),
+    "attn_fwd_noalloc": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i, _vp]),
     "attn_fwd_workspace_size": (_sz, [_i, _i, _i, _i, _i, _i]),
     "attn_fwd_num_splits": (_i, [_i, _i, _i, _i, _i, _i]),
     "attn_check_args": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i]),
@@ -139,6 +140,39 @@ def fwd(q, k, v, causal=False, scale=None, out=None, lse=None, num_splits=None, 
             workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
         wsz = 0 if workspace is None else workspace.numel() * workspace.element_size()
         _check("attn_fwd_ex", lib.attn_fwd_ex(*args, int(num_splits), _ptr(workspace), wsz, st))
+    return out, lse
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20   # ATTN_NOALLOC_SCRATCH_BYTES of include/attn.h
+
+
+def fwd_noalloc(q, k, v, causal=False, scale=None, out=None, lse=None):
+    """``fwd`` through ``attn_fwd_noalloc``: the library allocates nothing during the call.
+
+    A key-range split stages its partial results in the library's fixed device scratch array
+    (NOALLOC_SCRATCH_BYTES per GPU) instead of a fresh allocation; shapes whose split needs more
+    raise AttnError (ATTN_ERR_WORKSPACE). ``out`` and ``lse`` given by the caller keep this call
+    free of allocations on the Python side as well.
+    """
+    _need_gpu(q, k, v)
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, S, D]")
+    if not (q.dtype == k.dtype == v.dtype) or q.dtype not in _DTYPE:
+        raise ValueError("q, k, v must share one of float32/float16/bfloat16")
+    B, H, S_q, D = q.shape
+    S_k = k.shape[2]
+    if tuple(k.shape) != (B, H, S_k, D) or tuple(v.shape) != (B, H, S_k, D):
+        raise ValueError("k and v must be [B, H, S_k, D] matching q")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, S_q), dtype=torch.float32, device=q.device)
+    _need_gpu(out, lse)
+    _check("attn_fwd_noalloc", load().attn_fwd_noalloc(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, S_q, S_k, D, int(causal), float(scale),
+        _DTYPE[q.dtype], _stream(q.device)))
     return out, lse
 
 

@@ -5,6 +5,8 @@
 #include <stdio.h>
 #include <stdlib.h>
 
+#include <mutex>
+
 #include "../../include/attn.h"
 #include "common.h"
 #include "kernels.h"
@@ -158,6 +160,32 @@ int run_fwd(const void* q, const void* k, const void* v, void* o, float* lse, in
   return ATTN_OK;
 }
 
+// Scratch memory of attn_fwd_noalloc: a fixed device array in place of the
+// stream-ordered allocation attn_fwd makes for a key-range split. Each device
+// the library runs on holds its own copy until the process ends. Host code
+// never uses the array's name as an address (on the host it only stands for
+// the symbol): the device address comes from hipGetSymbolAddress, asked once
+// per device with that device current, and is kept per device.
+__device__ __align__(256) char scratch[ATTN_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_ptr[kMaxDevices];
+
+// Device address of the current device's scratch array, or nullptr if the
+// runtime cannot give it.
+void* device_scratch() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> g(scratch_mu);
+  if (scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return nullptr;
+    scratch_ptr[dev] = p;
+  }
+  return scratch_ptr[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -209,6 +237,24 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse
   const int rc = run_fwd(q, k, v, o, lse, B, H, S_q, S_k, D, causal, scale, dtype, num_splits,
                          workspace, workspace_bytes, false, (hipStream_t)stream);
   if (rc != ATTN_OK) say("attn_fwd_ex", rc);
+  return rc;
+}
+
+int attn_fwd_noalloc(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                     int S_q, int S_k, int D, int causal, float scale, int dtype, void* stream) {
+  int rc = check_args(q, k, v, o, lse, B, H, S_q, S_k, D, causal, scale, dtype);
+  // the split attn_fwd would choose must fit the fixed scratch array; this is
+  // decided on the host before anything touches the device
+  if (rc == ATTN_OK) {
+    const Plan p = plan_splits(dtype, B, H, S_q, S_k, D, 0);
+    if (ws_bytes(p, B, H, S_q, D) > (size_t)ATTN_NOALLOC_SCRATCH_BYTES) rc = ATTN_ERR_WORKSPACE;
+  }
+  void* ws = nullptr;
+  if (rc == ATTN_OK && (ws = device_scratch()) == nullptr) rc = ATTN_ERR_LAUNCH;
+  if (rc == ATTN_OK)
+    rc = run_fwd(q, k, v, o, lse, B, H, S_q, S_k, D, causal, scale, dtype, 0, ws, ATTN_NOALLOC_SCRATCH_BYTES,
+                 false, (hipStream_t)stream);
+  if (rc != ATTN_OK) say("attn_fwd_noalloc", rc);
   return rc;
 }
 

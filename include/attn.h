@@ -100,6 +100,30 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse
                 void* stream);
 
 /*
+ * attn_fwd_noalloc -- attn_fwd that allocates nothing, for callers that cannot
+ * allocate device memory during the call (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc).
+ *
+ * Same arguments, kernels, split choice, outputs and errors as attn_fwd, and
+ * the same bits. Where attn_fwd would take its key-range split workspace from
+ * the stream-ordered allocator, this entry point uses a fixed device array of
+ * ATTN_NOALLOC_SCRATCH_BYTES inside the library instead (one per GPU, held
+ * until the process ends; its address is looked up once per device on the
+ * first call, with the stream's device current). Shapes whose split needs
+ * more than that (attn_fwd_workspace_size(B, H, S_q, S_k, D, 0) above the
+ * limit) return ATTN_ERR_WORKSPACE before anything is enqueued; shapes that
+ * need no split never touch the array. Nothing in the array has to start at
+ * zero: every split writes its whole partial result before the merge reads
+ * it. All calls on one GPU share its array, so two calls that overlap in
+ * time on one GPU (on different streams, or from different host threads
+ * without ordering) race on it; calls ordered on one stream do not.
+ */
+#define ATTN_NOALLOC_SCRATCH_BYTES (16u << 20)
+int attn_fwd_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                     int B, int H, int S_q, int S_k, int D, int causal, float scale,
+                     int dtype, void* stream);
+
+/*
  * attn_fwd_persistent -- attn_fwd on a persistent grid: a fixed number of
  * workgroups, each resident on its own CU for the whole call, loops over the
  * (b, h, query tile) items dealt to it ([GN] "Weitere Optimierungen und

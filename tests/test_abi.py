@@ -179,3 +179,19 @@ def persistent(**kw):
 def test_persistent_validation_rejects(kw, code):
     """Host-side checks of attn_fwd_persistent: each bad argument is refused before the device is queried."""
     assert persistent(**kw) == code
+
+
+def test_noalloc_refuses_splits_beyond_its_scratch():
+    """attn_fwd_noalloc decides on the host, before touching the device, that a split needing more
+    than ATTN_NOALLOC_SCRATCH_BYTES cannot run; the decode workload's split fits."""
+    lib = attn.load()
+    B, H, S_q, S_k, D = 8, 32, 64, 8192, 128
+    assert attn.workspace_size(B, H, S_q, S_k, D) > attn.NOALLOC_SCRATCH_BYTES
+    rc = lib.attn_fwd_noalloc(P, P, P, P, P, B, H, S_q, S_k, D, 0, ctypes.c_float(0.125), attn.BF16, None)
+    assert rc == attn.ERR_WORKSPACE
+    # argument errors come first, as in attn_fwd
+    assert lib.attn_fwd_noalloc(None, P, P, P, P, B, H, S_q, S_k, D, 0, ctypes.c_float(0.125), attn.BF16,
+                                None) == attn.ERR_INVALID_ARG
+    assert 0 < attn.workspace_size(64, 32, 1, 32768, 128) <= attn.NOALLOC_SCRATCH_BYTES
+    hdr = open(HEADER).read()
+    assert f"#define ATTN_NOALLOC_SCRATCH_BYTES (16u << 20)" in hdr and attn.NOALLOC_SCRATCH_BYTES == 16 << 20
