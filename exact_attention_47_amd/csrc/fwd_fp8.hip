@@ -157,9 +157,13 @@ fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ K8, c
   }
 
   // stage j = K(j), V(j): every wave issues NI8 K and NI8 V loads (1 KiB =
-  // 8 rows each) on per-head buffer resources
-  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)Kh, (short)0, S_k * D8, 0x00020000);
-  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)Vh, (short)0, S_k * D8, 0x00020000);
+  // 8 rows each). Each stage has its own buffer resources, built in scalar
+  // registers: base at the tile's first row, range the bytes of K / V left
+  // from there (at most one tile). The per-lane offsets stay below one tile
+  // and are all the range check sees, so rows past the end (the last tile's
+  // tail, and the two stages fetched past the end so that every step issues
+  // the same loads and the wait counts stay exact) read zeros and touch no
+  // memory outside the tensors.
   int lane_k[NI8], lane_v[NI8];
 #pragma unroll
   for (int i = 0; i < NI8; i++) {
@@ -169,32 +173,20 @@ fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ K8, c
   }
   // (offsets and destinations go through locals: a target builtin with
   // template-dependent argument expressions is dropped from the host pass)
-  // The buffer range check covers the per-lane offset and not the scalar
-  // one, so the tile offset rides in the scalar part only for tiles wholly
-  // inside K and V. The last tiles (partial, and the two fetched past the
-  // end so that every step issues the same loads and the wait counts stay
-  // exact) put their whole offset in the per-lane part: those rows read
-  // zeros and touch no memory outside the tensors.
   auto issue_stage = [&](int j, char* base) {
-    const int soff = j * TILE8;
-    if ((j + 1) * BN8 <= S_k) {
+    const int off = j * TILE8;
+    const int left = S_k * D8 > off ? min(S_k * D8 - off, TILE8) : 0;
+    const __amdgpu_buffer_rsrc_t krs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(Kh + off), (short)0, left, 0x00020000);
+    const __amdgpu_buffer_rsrc_t vrs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(Vh + off), (short)0, left, 0x00020000);
 #pragma unroll
-      for (int i = 0; i < NI8; i++) {
-        char* kdst = base + (i * NW8 + wave) * 1024;
-        char* vdst = base + TILE8 + (i * NW8 + wave) * 1024;
-        const int lk = lane_k[i], lv = lane_v[i];
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (__attribute__((address_space(3))) void*)kdst, 16, lk, soff, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (__attribute__((address_space(3))) void*)vdst, 16, lv, soff, 0, 0);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < NI8; i++) {
-        char* kdst = base + (i * NW8 + wave) * 1024;
-        char* vdst = base + TILE8 + (i * NW8 + wave) * 1024;
-        const int lk = lane_k[i] + soff, lv = lane_v[i] + soff;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (__attribute__((address_space(3))) void*)kdst, 16, lk, 0, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (__attribute__((address_space(3))) void*)vdst, 16, lv, 0, 0, 0);
-      }
+    for (int i = 0; i < NI8; i++) {
+      char* kdst = base + (i * NW8 + wave) * 1024;
+      char* vdst = base + TILE8 + (i * NW8 + wave) * 1024;
+      const int lk = lane_k[i], lv = lane_v[i];
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (__attribute__((address_space(3))) void*)kdst, 16, lk, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (__attribute__((address_space(3))) void*)vdst, 16, lv, 0, 0, 0);
     }
   };
 

@@ -242,9 +242,12 @@ fwd_mfma_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
   // row and 1 KiB block) is wave-uniform: no vector arithmetic per load.
   // The buffer range check covers the per-lane offset and not the scalar
   // one, so that split serves only tiles that lie wholly inside K and V. A
-  // tile that reaches past the last row puts its whole offset in the
-  // per-lane part: the rows past the end then read zeros (their scores are
-  // masked, and zero V rows keep 0 * V finite whatever memory follows).
+  // tile that reaches past the last row gets one resource per load
+  // instruction instead, built in scalar registers: its base is the
+  // instruction's first row and its range the bytes left after it, so the
+  // per-lane offset alone is checked and the rows past the end read zeros
+  // (their scores are masked, and zero V rows keep 0 * V finite whatever
+  // memory follows).
   // (packed rows are strided: the range ends after the last row's D elements)
   const int kv_bytes = VARLEN ? (S_k > 0 ? (S_k - 1) * RBg + C::RB : 0) : S_k * C::RB;
   const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)Kh, (short)0, kv_bytes, 0x00020000);
@@ -259,7 +262,7 @@ fwd_mfma_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
   }
   // (offsets and destinations go through locals: a target builtin with
   // template-dependent argument expressions is dropped from the host pass)
-  auto load_tile = [&](__amdgpu_buffer_rsrc_t rs, int lane_off, int row0, char* tb) {
+  auto load_tile = [&](__amdgpu_buffer_rsrc_t rs, const T* head, int lane_off, int row0, char* tb) {
     if (row0 + C::BN <= S_k) {
 #pragma unroll
       for (int i = 0; i < 2 * C::NI; i++) {
@@ -274,16 +277,19 @@ fwd_mfma_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
       for (int i = 0; i < 2 * C::NI; i++) {
         const int blk = i * 4 + wave;
         char* dst = tb + blk * 1024;
-        const int voff = lane_off + (row0 + blk * C::RPI) * RBg;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)dst, 16, voff,
+        const int off = (row0 + blk * C::RPI) * RBg;
+        const int left = kv_bytes > off ? kv_bytes - off : 0;
+        const __amdgpu_buffer_rsrc_t r1 =
+            __builtin_amdgcn_make_buffer_rsrc((void*)((const char*)head + off), (short)0, left, 0x00020000);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r1, (__attribute__((address_space(3))) void*)dst, 16, lane_off,
                                                  0, 0, 0);
       }
     }
   };
   auto issue_stage = [&](int s) {
     char* base = lds + (s & 1) * C::STAGE;
-    if (s < n_tiles) load_tile(krs, lane_k, k_lo + s * C::BN, base);
-    if (s >= 1 && s - 1 < n_tiles) load_tile(vrs, lane_v, k_lo + (s - 1) * C::BN, base + C::TILE);
+    if (s < n_tiles) load_tile(krs, Kh, lane_k, k_lo + s * C::BN, base);
+    if (s >= 1 && s - 1 < n_tiles) load_tile(vrs, Vh, lane_v, k_lo + (s - 1) * C::BN, base + C::TILE);
   };
 
   // ---- per-lane LDS read offsets (swizzle folded in)
