@@ -42,5 +42,6 @@ from .fp8 import (  # noqa: F401
     hadamard_quantize,
     dequantize_blocks,
 )
-from .fp8_pipeline import fp8_attention_sim, rmse  # noqa: F401
+from .fp8_pipeline import (  # noqa: F401
+    fp8_attention_sim, fp8_attention_rows, p_rounding_bound, round_p, rmse, P_EXP_RANGE)
 from .rope import rope_angles, rotary, rotary_f32, rope_hadamard_quantize  # noqa: F401

@@ -127,10 +127,19 @@ def hadamard_quantize(x, signs, block_rows: int = 64):
     return codes, scales
 
 
-def quantize_per_tensor(x):
-    """One scale for the whole tensor: (codes uint8, scale float32 scalar)."""
+def quantize_per_tensor(x, amax=None):
+    """One scale for the whole tensor: (codes uint8, scale float32 scalar).
+
+    ``amax``, when given, is max |x| over the whole tensor of which x holds
+    only a part (for example some heads); by default it is taken from x.
+    """
     x32 = np.asarray(x, dtype=np.float32)
-    a = np.float32(np.abs(x32).max()) if x32.size else np.float32(0)
+    if amax is not None:
+        a = np.float32(amax)
+        if x32.size and not np.float32(np.abs(x32).max()) <= a:
+            raise ValueError("amax is smaller than max |x|")
+    else:
+        a = np.float32(np.abs(x32).max()) if x32.size else np.float32(0)
     if a == 0:
         return np.zeros(x32.shape, dtype=np.uint8), np.float32(1)
     inv = np.float32(np.float32(E4M3_MAX) / a)

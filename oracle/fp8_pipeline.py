@@ -17,14 +17,24 @@ transformations"):
   scales (``oracle.fp8.hadamard_quantize``); V -> one per-tensor scale.
 * ``"per_tensor"``: Q, K, V -> one per-tensor scale each, no transform.
 
-Attention is then the float64 definition on the dequantized values. With
-``p_quant`` the probabilities entering the P V product are also rounded to
-E4M3 after multiplication by 2^8 (and divided by 2^8 again), with the row sum
-taken from the unrounded probabilities, the reading used by the FP8 kernel.
+Attention is then the float64 definition on the dequantized values.
+
+The pages do not say how the probabilities enter the FP8 P V product. Reading:
+each p (relative to its row's maximum) is multiplied by 2^k, rounded to E4M3
+and divided by 2^k again, while the row sum l is taken from the unrounded p
+(``round_p``). The factor keeps small p out of the E4M3 subnormals. A kernel
+that forms p against a running reference which trails the row's final maximum
+by up to tau (log2) and scales by 2^k0 uses, relative to the final maximum,
+factors between 2^k0 and 2^(k0 + tau); the FP8 kernel of this repository has
+k0 = 7 and tau = 1.75. The simulation takes one factor 2^k for the whole row
+against the row's final maximum (no tiling); evaluated at k = 7 and k = 8.75
+it brackets that kernel's rounding. ``p_rounding_bound`` gives the largest
+error the rounding of P can cause in each output element for any k >= 7.
 
 Parity unpinned: the absolute error values of this simulation are not printed
 by the pages; only the ratio between the two schemes is (2.6x), and that ratio
-is what ``tests/test_oracle.py`` pins.
+is what ``tests/test_oracle.py`` pins, together with worked values of
+``round_p`` and the bound.
 """
 
 from __future__ import annotations
@@ -35,7 +45,8 @@ from .attention import allowed_mask
 from .fp8 import (dequantize_blocks, e4m3_decode, e4m3_encode, hadamard_quantize,
                   quantize_per_tensor)
 
-P_SHIFT = 256.0   # 2^8: keeps probabilities out of the E4M3 subnormal range
+P_EXP = 7.0        # default k of round_p: p * 2^7 keeps small p out of the E4M3 subnormals
+P_EXP_RANGE = (7.0, 8.75)   # the factors a running reference trailing the maximum by <= 1.75 gives
 
 
 def rmse(a, b) -> float:
@@ -44,8 +55,51 @@ def rmse(a, b) -> float:
     return float(np.sqrt(np.mean((a - b) ** 2)))
 
 
-def dequantized_inputs(q, k, v, scheme: str, signs=None, block_rows: int = 64):
-    """Quantize then dequantize Q, K, V under ``scheme``; returns float64 arrays."""
+def round_p(p, p_exp: float = P_EXP) -> np.ndarray:
+    """E4M3(p * 2^p_exp) / 2^p_exp in float64: a probability as the P V product takes it.
+
+    The product p * 2^p_exp is rounded once (nearest, ties to even, from its
+    float64 value) and scaled back; no saturation is reached for p <= 1 and
+    p_exp <= log2(448).
+    """
+    f = np.exp2(np.float64(p_exp))
+    return e4m3_decode(e4m3_encode(np.asarray(p, dtype=np.float64) * f)) / f
+
+
+def p_rounding_bound(qh, kh, vh, causal: bool, scale: float) -> np.ndarray:
+    """Largest |O error| that rounding P with ``round_p`` can cause, per output element.
+
+    For p * 2^k in the E4M3 normal range (>= 2^-6) rounding to nearest moves it
+    by at most half a step, 2^-4 of its value (three mantissa bits); below that
+    the step is 2^-9, so p moves by at most 2^-10 / 2^k <= 2^-17 for k >= 7. With
+    l from the unrounded p, O_id = sum_j p_ij V_jd / l_i therefore moves by at
+    most sum_j b(p_ij) |V_jd| / l_i with b(p) = 2^-4 p for p >= 2^-13 and 2^-17
+    below. qh, kh, vh are the dequantized [B, H, S, D] inputs.
+    """
+    qh, kh, vh = (np.asarray(x, dtype=np.float64) for x in (qh, kh, vh))
+    b, h, s_q, _ = qh.shape
+    s_k = kh.shape[2]
+    out = np.empty((b, h, s_q, vh.shape[3]))
+    allowed = allowed_mask(s_q, s_k, causal)
+    for bi in range(b):
+        for hi in range(h):
+            s = scale * (qh[bi, hi] @ kh[bi, hi].T)
+            s = np.where(allowed, s, -np.inf)
+            p = np.exp(s - s.max(axis=1)[:, None])
+            l = p.sum(axis=1)
+            bp = np.where(p >= 2.0 ** -13, p / 16.0, np.where(p > 0, 2.0 ** -17, 0.0))
+            out[bi, hi] = (bp @ np.abs(vh[bi, hi])) / l[:, None]
+    return out
+
+
+def dequantized_inputs(q, k, v, scheme: str, signs=None, block_rows: int = 64, amax=None):
+    """Quantize then dequantize Q, K, V under ``scheme``; returns float64 arrays.
+
+    ``amax`` (optional) gives the per-tensor maxima {"q": a, "k": a, "v": a} of
+    the whole tensors when q, k, v are only some of their heads; block scales
+    depend on each head's own rows and need nothing more.
+    """
+    am = amax or {}
     if scheme == "hadamard":
         if signs is None:
             raise ValueError("hadamard scheme needs a sign vector")
@@ -54,43 +108,54 @@ def dequantized_inputs(q, k, v, scheme: str, signs=None, block_rows: int = 64):
         qh = dequantize_blocks(qc, qs, block_rows)
         kh = dequantize_blocks(kc, ks, block_rows)
     elif scheme == "per_tensor":
-        qc, qs = quantize_per_tensor(q)
-        kc, ks = quantize_per_tensor(k)
+        qc, qs = quantize_per_tensor(q, am.get("q"))
+        kc, ks = quantize_per_tensor(k, am.get("k"))
         qh = e4m3_decode(qc) * np.float64(qs)
         kh = e4m3_decode(kc) * np.float64(ks)
     else:
         raise ValueError(f"unknown scheme {scheme!r}")
-    vc, vs = quantize_per_tensor(v)
+    vc, vs = quantize_per_tensor(v, am.get("v"))
     vh = e4m3_decode(vc) * np.float64(vs)
     return qh, kh, vh
 
 
 def fp8_attention_sim(q, k, v, causal: bool, scale: float, scheme: str, signs=None,
-                      block_rows: int = 64, p_quant: bool = True):
+                      block_rows: int = 64, p_quant: bool = True, p_exp: float = P_EXP):
     """Simulated FP8 attention output (float64 O, LSE) under ``scheme``.
 
     When the Hadamard scheme is used the dequantized Q and K are in the
     rotated basis; Q K^T is the same as in the original basis up to
     quantization error, and V is never rotated, so O is directly comparable
-    with exact attention on the original inputs.
+    with exact attention on the original inputs. With ``p_quant`` the
+    probabilities entering P V are ``round_p(p, p_exp)`` against the row's
+    final maximum; l and the LSE use the unrounded p.
     """
     qh, kh, vh = dequantized_inputs(q, k, v, scheme, signs, block_rows)
     b, h, s_q, d = qh.shape
-    s_k = kh.shape[2]
     o = np.empty((b, h, s_q, vh.shape[3]))
     lse = np.empty((b, h, s_q))
-    allowed = allowed_mask(s_q, s_k, causal)
+    rows = np.arange(s_q)
     for bi in range(b):
         for hi in range(h):
-            s = scale * (qh[bi, hi] @ kh[bi, hi].T)
-            s = np.where(allowed, s, -np.inf)
-            m = s.max(axis=1)
-            p = np.exp(s - m[:, None])
-            l = p.sum(axis=1)
-            if p_quant:
-                pq = e4m3_decode(e4m3_encode((p * P_SHIFT).astype(np.float32))) / P_SHIFT
-            else:
-                pq = p
-            o[bi, hi] = (pq @ vh[bi, hi]) / l[:, None]
-            lse[bi, hi] = m + np.log(l)
+            o[bi, hi], lse[bi, hi] = fp8_attention_rows(qh[bi, hi], kh[bi, hi], vh[bi, hi], rows, causal,
+                                                        scale, s_q, p_quant, p_exp)
     return o, lse
+
+
+def fp8_attention_rows(qh, kh, vh, rows, causal: bool, scale: float, s_q: int, p_quant: bool = True,
+                       p_exp: float = P_EXP):
+    """Query rows ``rows`` of the simulated FP8 attention of one (b, h).
+
+    qh [S_q, D], kh [S_k, D], vh [S_k, D] are the dequantized inputs of that
+    head; returns (O rows float64, LSE rows). Same arithmetic as
+    ``fp8_attention_sim``.
+    """
+    qh, kh, vh = (np.asarray(x, dtype=np.float64) for x in (qh, kh, vh))
+    rows = np.asarray(rows)
+    s = scale * (qh[rows] @ kh.T)
+    s = np.where(allowed_mask(s_q, kh.shape[0], causal, rows), s, -np.inf)
+    m = s.max(axis=1)
+    p = np.exp(s - m[:, None])
+    l = p.sum(axis=1)
+    pq = round_p(p, p_exp) if p_quant else p
+    return (pq @ vh) / l[:, None], m + np.log(l)

@@ -413,9 +413,71 @@ def test_fp8_sim_p_rounding_is_a_small_perturbation():
     sg = inputs.signs(d, 2).numpy()
     ref, _ = oracle.attention(q, k, v, False, 0.125)
     o0, _ = oracle.fp8_attention_sim(q, k, v, False, 0.125, "hadamard", sg, p_quant=False)
-    o1, _ = oracle.fp8_attention_sim(q, k, v, False, 0.125, "hadamard", sg, p_quant=True)
-    e0, e1 = oracle.rmse(o0, ref), oracle.rmse(o1, ref)
-    assert e0 <= e1 < 1.3 * e0
+    e0 = oracle.rmse(o0, ref)
+    for k_exp in oracle.P_EXP_RANGE:
+        o1, _ = oracle.fp8_attention_sim(q, k, v, False, 0.125, "hadamard", sg, p_quant=True, p_exp=k_exp)
+        e1 = oracle.rmse(o1, ref)
+        assert e0 <= e1 < 1.3 * e0, (k_exp, e0, e1)
+
+
+def test_round_p_worked_values():
+    """E4M3 steps are 4 in [32, 64), 16 in [128, 256), 32 in [256, 448]; the smallest subnormal is 2^-9."""
+    rp = oracle.round_p
+    assert rp(0.3, 7) == 40 / 128                       # 38.4 -> 40
+    assert rp(38 / 128, 7) == 40 / 128                  # tie 36 | 40 -> the even code (40)
+    assert rp(34 / 128, 7) == 32 / 128                  # tie 32 | 36 -> the even code (32)
+    assert rp(1.0, 7) == 1.0 and rp(40 / 128, 7) == 40 / 128   # already E4M3 values: unchanged
+    f = 2.0 ** 8.75
+    assert rp(0.3, 8.75) == 128 / f                     # 129.16 -> 128
+    assert rp(1.0, 8.75) == 416 / f                     # 430.54 -> 416 (448 is farther)
+    assert rp(2.0 ** -16, 7) == 2.0 ** -16              # p * 2^7 = 2^-9, the smallest subnormal
+    assert rp(1.4 * 2.0 ** -17, 7) == 2.0 ** -16        # 0.7 * 2^-9 -> 2^-9
+    assert rp(0.4 * 2.0 ** -16, 7) == 0.0               # 0.4 * 2^-9 -> 0
+    assert rp(0.0, 7) == 0.0
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_sim_p_quant_exact_when_every_p_is_an_e4m3_value(causal):
+    """Q = 0: every allowed p is 1, and 1 * 2^7 is an E4M3 value, so rounding P changes no bit."""
+    q = np.zeros((1, 2, 40, 64), np.float32)
+    k = inputs.normal((1, 2, 70, 64), 3, inputs.TENSOR_K).float().numpy()
+    v = inputs.normal((1, 2, 70, 64), 3, inputs.TENSOR_V).float().numpy()
+    sg = inputs.signs(64, 3).numpy()
+    o0, l0 = oracle.fp8_attention_sim(q, k, v, causal, 0.125, "hadamard", sg, p_quant=False)
+    o1, l1 = oracle.fp8_attention_sim(q, k, v, causal, 0.125, "hadamard", sg, p_quant=True, p_exp=7.0)
+    assert np.array_equal(o0, o1) and np.array_equal(l0, l1)
+
+
+def test_p_rounding_bound_holds_and_is_reached():
+    """The bound holds element by element for every factor 2^k, k in [7, 8.75], and is not loose by
+    orders of magnitude (a dropped 1/l or a missing |V| would break one of the two checks)."""
+    b, h, s, d = 1, 2, 300, 64
+    q, k, v = inputs.qkv(b, h, s, s, d, seed=4, dtype=torch.bfloat16, outliers=True)
+    q, k, v = (x.float().numpy() for x in (q, k, v))
+    sg = inputs.signs(d, 4).numpy()
+    qh, kh, vh = oracle.fp8_pipeline.dequantized_inputs(q, k, v, "hadamard", sg)
+    for causal in (False, True):
+        ref, _ = oracle.attention(qh, kh, vh, causal, 0.125)
+        bound = oracle.p_rounding_bound(qh, kh, vh, causal, 0.125)
+        for k_exp in (7.0, 7.5, 8.0, 8.75):
+            sim, _ = oracle.fp8_attention_sim(q, k, v, causal, 0.125, "hadamard", sg, p_exp=k_exp)
+            err = np.abs(sim - ref)
+            assert np.all(err <= bound * (1 + 1e-9) + 1e-15), k_exp
+            assert err.max() > 0.05 * bound.max()
+
+
+def test_p_rounding_bound_catches_a_planted_mistake():
+    """A P rounding that forgets to scale back by 2^k breaks the bound at once."""
+    b, h, s, d = 1, 1, 64, 64
+    q, k, v = inputs.qkv(b, h, s, s, d, seed=5, dtype=torch.bfloat16)
+    qh, kh, vh = (x.float().numpy().astype(np.float64) for x in (q, k, v))
+    ref, _ = oracle.attention(qh, kh, vh, False, 0.125)
+    bound = oracle.p_rounding_bound(qh, kh, vh, False, 0.125)
+    sc = 0.125 * (qh[0, 0] @ kh[0, 0].T)
+    p = np.exp(sc - sc.max(axis=1)[:, None])
+    wrong = oracle.e4m3_decode(oracle.e4m3_encode(p * 128.0)) / 1.0   # 2^7 not undone
+    o_wrong = (wrong @ vh[0, 0]) / p.sum(axis=1)[:, None]
+    assert np.any(np.abs(o_wrong - ref[0, 0]) > bound[0, 0])
 
 
 # ---------------------------------------------------------------- packed (variable-length) batches
