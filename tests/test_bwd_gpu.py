@@ -83,6 +83,25 @@ def test_bwd_fullsize_two_heads(gpu_lib):
         check(f"dV b{b}h{h}", dv[b:b + 1, h:h + 1], rv)
 
 
+@pytest.mark.parametrize("B,H,S,D,causal", [(2, 16, 8192, 128, False), (2, 16, 8192, 128, True),
+                                            (4, 32, 4096, 64, False), (4, 32, 4096, 64, True)],
+                         ids=["B2H16S8K_D128_n", "B2H16S8K_D128_c", "B4H32S4K_D64_n", "B4H32S4K_D64_c"])
+def test_bwd_bench_workloads_two_heads(gpu_lib, B, H, S, D, causal):
+    """The backward workloads the bench times (same seed, inputs and launch), two whole heads against
+    the oracle: the first and the last (b, h), which sit on different XCDs and, when causal, take the
+    heaviest-first deal's first and last outer blocks."""
+    note(f"bwd bench workload B{B} H{H} S{S} D{D} causal={causal}")
+    q, k, v, do, scale, dq, dk, dv = run_case(gpu_lib, B, H, S, S, D, causal, torch.bfloat16, 0)
+    for b, h in ((0, 0), (B - 1, H - 1)):
+        rq, rk, rv = oracle.attention_backward(q[b:b + 1, h:h + 1].float().cpu().numpy(),
+                                               k[b:b + 1, h:h + 1].float().cpu().numpy(),
+                                               v[b:b + 1, h:h + 1].float().cpu().numpy(),
+                                               do[b:b + 1, h:h + 1].float().cpu().numpy(), causal, scale)
+        check(f"dQ b{b}h{h}", dq[b:b + 1, h:h + 1], rq)
+        check(f"dK b{b}h{h}", dk[b:b + 1, h:h + 1], rk)
+        check(f"dV b{b}h{h}", dv[b:b + 1, h:h + 1], rv)
+
+
 def test_bwd_is_deterministic(gpu_lib):
     note("bwd determinism")
     q, k, v, do, scale, dq, dk, dv = run_case(gpu_lib, 1, 4, 500, 500, 128, True, torch.bfloat16, 5)
