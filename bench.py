@@ -13,9 +13,15 @@ kernel (its average launch duration from HIP events recorded on the stream it
 runs on, inside the timed region), the CPU oracle timed on a bounded sample,
 and (unless --no-extras) the other configured workloads as extra figures: the
 D=64 non-causal and D=128 causal sweeps over S = 512..16K, the D=256 causal 8K
-shape, the S_q=1 / S_k=32K decode shape with its key-range split, and the FP8
+shape, the S_q=1 / S_k=32K decode shape with its key-range split, the FP8
 pipeline (Hadamard + block quantization, per-tensor V quantization, FP8
-attention) with its error against exact attention.
+attention), packed batches, the backward pass and the persistent grid.
+
+Unless --no-cpu-baseline: the CPU oracle timed on a sample of the headline
+workload, and the FP8 error on the outlier workload (B=2 H=16 S=8K D=128): the
+RMSE of the FP8 pipeline with the Hadamard transform and of plain per-tensor
+FP8, each against exact attention (the oracle) on sampled rows, and their
+ratio. That leg is the only one that calls the oracle.
 """
 
 from __future__ import annotations
@@ -226,6 +232,46 @@ def cpu_baseline(B, H, S, D, causal, heads=32):
                       f"({S}x{S} scores, D={D}): {dt:.2f} s"}
 
 
+def fp8_accuracy(heads=((0, 0), (1, 15), (0, 7), (1, 3)), rows_per_head=48):
+    """FP8 error on the outlier workload (B=2 H=16 S=8K D=128, non-causal) against exact attention.
+
+    The Hadamard + 64-row block pipeline and plain per-tensor FP8 (no transform) run on the GPU; the
+    oracle gives exact attention on the unquantized inputs for sampled query rows of a few heads.
+    """
+    import numpy as np
+    import oracle
+    B, H, S, D = 2, 16, 8192, 128
+    scale = 1 / math.sqrt(D)
+    q, k, v = inputs.qkv(B, H, S, S, D, seed=0, dtype=torch.bfloat16, device="cuda", outliers=True)
+    sg = inputs.signs(D, 0).cuda()
+    q8, qs = attn.hadamard_quant(q, sg)
+    k8, ks = attn.hadamard_quant(k, sg)
+    v8, vs = attn.quant_per_tensor(v)
+    o_h, _ = attn.fwd_fp8(q8, k8, v8, qs, ks, vs, False, scale)
+    q8p, qsp = attn.quant_per_tensor(q)
+    k8p, ksp = attn.quant_per_tensor(k)
+    o_p, _ = attn.fwd_fp8(q8p, k8p, v8, qsp.expand(B, H, S // 64).contiguous(),
+                          ksp.expand(B, H, S // 64).contiguous(), vs, False, scale)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(3)
+    d_h, d_p = [], []
+    for b, h in heads:
+        rows = np.sort(rng.choice(S, size=rows_per_head, replace=False))
+        ridx = torch.from_numpy(rows).cuda()
+        ref, _ = oracle.attention_rows(q[b, h, ridx].float().cpu().numpy(), k[b, h].float().cpu().numpy(),
+                                       v[b, h].float().cpu().numpy(), rows, False, scale, s_q=S)
+        d_h.append(o_h[b, h, ridx].float().cpu().numpy() - ref)
+        d_p.append(o_p[b, h, ridx].float().cpu().numpy() - ref)
+    e_h = float(np.sqrt(np.mean(np.concatenate(d_h) ** 2)))
+    e_p = float(np.sqrt(np.mean(np.concatenate(d_p) ** 2)))
+    del q, k, v, q8, k8, v8, o_h, o_p, q8p, k8p
+    torch.cuda.empty_cache()
+    return {"rmse_hadamard": round(e_h, 6), "rmse_plain": round(e_p, 6), "ratio": round(e_p / e_h, 3),
+            "target": "rmse_hadamard <= 0.5 * rmse_plain", "met": bool(e_h <= 0.5 * e_p),
+            "sample": f"{rows_per_head} query rows in each of {len(heads)} heads, against the oracle's exact "
+                      f"attention on the unquantized inputs (N(0,1), 0.1 % N(0,10) outliers, seed 0)"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -348,6 +394,7 @@ def main():
         out["extras"] = extras
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(B, H, S, D, causal)
+        out["fp8_accuracy"] = fp8_accuracy()
     print(json.dumps(out), flush=True)
 
 
