@@ -38,7 +38,7 @@ _SIGS = {
     "attn_fwd_ex": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i, _i, _vp, _sz, _vp]),
     "attn_fwd_noalloc": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i, _vp]),
     "attn_fwd_workspace_size": (_sz, [_i, _i, _i, _i, _i, _i]),
-    "attn_fwd_num_splits": (_i, [_i, _i, _i, _i, _i, _i]),
+    "attn_fwd_num_splits": (_i, [_i, _i, _i, _i, _i, _i, _i]),
     "attn_check_args": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i]),
     "hadamard_quant": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp]),
     "quant_per_tensor": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp]),
@@ -101,8 +101,9 @@ def workspace_size(B, H, S_q, S_k, D, num_splits=0) -> int:
     return int(load().attn_fwd_workspace_size(B, H, S_q, S_k, D, num_splits))
 
 
-def num_splits(B, H, S_q, S_k, D, num_splits=0) -> int:
-    return int(load().attn_fwd_num_splits(B, H, S_q, S_k, D, num_splits))
+def num_splits(B, H, S_q, S_k, D, num_splits=0, dtype=BF16) -> int:
+    """The split count attn_fwd (or attn_fwd_ex with num_splits) uses for these sizes and element type."""
+    return int(load().attn_fwd_num_splits(B, H, S_q, S_k, D, int(dtype), num_splits))
 
 
 def fwd(q, k, v, causal=False, scale=None, out=None, lse=None, num_splits=None, workspace=None):

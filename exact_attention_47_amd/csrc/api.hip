@@ -209,9 +209,10 @@ int attn_check_args(const void* q, const void* k, const void* v, const void* o, 
   return check_args(q, k, v, o, lse, B, H, S_q, S_k, D, causal, scale, dtype);
 }
 
-int attn_fwd_num_splits(int B, int H, int S_q, int S_k, int D, int num_splits) {
+int attn_fwd_num_splits(int B, int H, int S_q, int S_k, int D, int dtype, int num_splits) {
   if (B <= 0 || H <= 0 || S_q <= 0 || S_k <= 0 || num_splits < 0) return 1;
-  return plan_splits(ATTN_BF16, B, H, S_q, S_k, D, num_splits).n_split;
+  if (dtype != ATTN_F32 && dtype != ATTN_F16 && dtype != ATTN_BF16) return 1;
+  return plan_splits(dtype, B, H, S_q, S_k, D, num_splits).n_split;
 }
 
 size_t attn_fwd_workspace_size(int B, int H, int S_q, int S_k, int D, int num_splits) {

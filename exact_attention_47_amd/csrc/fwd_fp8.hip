@@ -40,6 +40,11 @@
 //   more than 1.75 (log2), which keeps p * 2^7 <= 430 < 448; at each move the
 //   row's largest p is exactly 2^7, which E4M3 holds without rounding.
 //
+// * V comes as [S_k, D] codes (read transposed in flight, below) or, with
+//   v_transposed, as [D, S_k] codes: those tiles are stored [128 d][64 keys]
+//   and read with eight 4-byte loads per fragment, dword q holding keys
+//   8q + 4h .. 8q + 4h + 3 (the P fragment's k order, below).
+//
 // * The transposed V read picks, for element r of read p, the key row that
 //   the P fragment holds in that k slot: P^T slot t of lane half h is key
 //   32(t/16) + 8((t%16)/4) + 4h + t%4 (the S^T accumulator order), and
@@ -93,7 +98,11 @@ __device__ __forceinline__ uint32_t pack_fp8(float a, float b, float c, float d)
 
 template <int N> struct IC8 { static constexpr int value = N; };
 
-template <bool CAUSAL>
+// V^T tiles ([128 d][64 keys], VT = true): 16-byte chunk c of row d sits
+// at chunk position c ^ vt8_swz(d)
+__device__ __forceinline__ int vt8_swz(int d) { return (d >> 2) & 3; }
+
+template <bool CAUSAL, bool VT>
 __global__ void __launch_bounds__(NT8)
 __attribute__((amdgpu_waves_per_eu(3, 3)))
 fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ K8, const uint8_t* __restrict__ V8,
@@ -169,8 +178,19 @@ fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ K8, c
   for (int i = 0; i < NI8; i++) {
     const int r = (i * NW8 + wave) * 8 + (lane >> 3);
     lane_k[i] = r * D8 + (((lane & 7) ^ k8_swz(r)) * 16);
-    lane_v[i] = r * D8 + (((lane & 7) ^ v8_swz(r)) * 16);
+    if (VT) {
+      // V^T [D][S_k] per head: a 1 KiB wave load fills 16 rows d of 64 key
+      // bytes; the tile's key offset (64 j) is added per stage
+      const int d = (i * NW8 + wave) * 16 + (lane >> 2);
+      lane_v[i] = d * S_k + (((lane & 3) ^ vt8_swz(d)) * 16);
+    } else {
+      lane_v[i] = r * D8 + (((lane & 7) ^ v8_swz(r)) * 16);
+    }
   }
+  // V^T: one resource over the head's D rows of S_k bytes. Key bytes past
+  // S_k in a tile belong to the next row (finite codes whose P is 0); past
+  // the last row the range check returns zeros.
+  const __amdgpu_buffer_rsrc_t vtrs = __builtin_amdgcn_make_buffer_rsrc((void*)Vh, (short)0, D8 * S_k, 0x00020000);
   // (offsets and destinations go through locals: a target builtin with
   // template-dependent argument expressions is dropped from the host pass)
   auto issue_stage = [&](int j, char* base) {
@@ -186,7 +206,13 @@ fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ K8, c
       char* vdst = base + TILE8 + (i * NW8 + wave) * 1024;
       const int lk = lane_k[i], lv = lane_v[i];
       __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (__attribute__((address_space(3))) void*)kdst, 16, lk, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (__attribute__((address_space(3))) void*)vdst, 16, lv, 0, 0, 0);
+      if (VT) {
+        const int lvt = lv + j * BN8;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vtrs, (__attribute__((address_space(3))) void*)vdst, 16, lvt, 0, 0,
+                                                 0);
+      } else {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (__attribute__((address_space(3))) void*)vdst, 16, lv, 0, 0, 0);
+      }
     }
   };
 
@@ -202,8 +228,15 @@ fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ K8, c
   const int xv = v8_swz(vrow);
   int v_rd[DB8];
 #pragma unroll
-  for (int db = 0; db < DB8; db++)
-    v_rd[db] = vrow * D8 + (((2 * db + (g & 1)) ^ xv) * 16) + 8 * (jj & 1);
+  for (int db = 0; db < DB8; db++) {
+    if (VT) {
+      // V^T row d = 32 db + nn, chunk db: dword q of the fragment holds keys
+      // 8 q + 4 h .. +3, byte 8 (q & 1) + 4 h of chunk q / 2
+      v_rd[db] = nn * BN8 + ((db ^ vt8_swz(nn)) * 16) + 4 * hh;
+    } else {
+      v_rd[db] = vrow * D8 + (((2 * db + (g & 1)) ^ xv) * 16) + 8 * (jj & 1);
+    }
+  }
 
   v16f o[DB8];
 #pragma unroll
@@ -312,6 +345,14 @@ fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ K8, c
     {
       const char* vl = rbuf + TILE8;
       auto load = [&](int db) {
+        if (VT) {
+          // rows 32 db + nn of the V^T tile; v_rd holds the chunk of q / 2 = c
+          const char* row = vl + db * 32 * BN8;
+          v8i r;
+#pragma unroll
+          for (int q = 0; q < 8; q++) r[q] = *(const int*)(row + v_rd[q >> 1] + 8 * (q & 1));
+          return r;
+        }
         v2i part[4];
 #pragma unroll
         for (int p = 0; p < 4; p++) {
@@ -395,19 +436,29 @@ fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ K8, c
 
 }  // namespace
 
+template <bool CAUSAL, bool VT>
+static void launch_fp8(dim3 grid, hipStream_t st, const void* q8, const void* k8, const void* v8, const float* qs,
+                       const float* ks, const float* vs, void* o, float* lse, int BH, int S_q, int S_k, int n_qt,
+                       float c) {
+  hipLaunchKernelGGL((fwd_fp8_kernel<CAUSAL, VT>), grid, dim3(NT8), 0, st, (const uint8_t*)q8, (const uint8_t*)k8,
+                     (const uint8_t*)v8, qs, ks, vs, (__bf16*)o, lse, BH, S_q, S_k, n_qt, c);
+}
+
 hipError_t launch_fwd_fp8(const void* q8, const void* k8, const void* v8, const float* qs, const float* ks,
                           const float* vs, void* o, float* lse, int B, int H, int S_q, int S_k, int D,
                           int causal, float c, int v_transposed, hipStream_t st) {
-  if (D != D8 || v_transposed) return hipErrorNotSupported;
+  if (D != D8) return hipErrorNotSupported;
+  if (v_transposed && S_k % 16 != 0) return hipErrorNotSupported;            // 16-byte aligned V^T rows
   if ((long long)(S_k + 4 * BN8) * D8 > 0x7fffffffLL) return hipErrorInvalidValue;   // 32-bit buffer offsets
   const int n_qt = (S_q + BM8 - 1) / BM8;
   const dim3 grid((unsigned)(B * H * n_qt));
-  if (causal)
-    hipLaunchKernelGGL(fwd_fp8_kernel<true>, grid, dim3(NT8), 0, st, (const uint8_t*)q8, (const uint8_t*)k8,
-                       (const uint8_t*)v8, qs, ks, vs, (__bf16*)o, lse, B * H, S_q, S_k, n_qt, c);
-  else
-    hipLaunchKernelGGL(fwd_fp8_kernel<false>, grid, dim3(NT8), 0, st, (const uint8_t*)q8, (const uint8_t*)k8,
-                       (const uint8_t*)v8, qs, ks, vs, (__bf16*)o, lse, B * H, S_q, S_k, n_qt, c);
+  if (causal) {
+    if (v_transposed) launch_fp8<true, true>(grid, st, q8, k8, v8, qs, ks, vs, o, lse, B * H, S_q, S_k, n_qt, c);
+    else launch_fp8<true, false>(grid, st, q8, k8, v8, qs, ks, vs, o, lse, B * H, S_q, S_k, n_qt, c);
+  } else {
+    if (v_transposed) launch_fp8<false, true>(grid, st, q8, k8, v8, qs, ks, vs, o, lse, B * H, S_q, S_k, n_qt, c);
+    else launch_fp8<false, false>(grid, st, q8, k8, v8, qs, ks, vs, o, lse, B * H, S_q, S_k, n_qt, c);
+  }
   return hipGetLastError();
 }
 

@@ -32,7 +32,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 1
+#define ATTN_ABI_VERSION 2
 
 /* element types */
 #define ATTN_F32  0
@@ -212,9 +212,13 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
  * (0 when the effective split count is 1). num_splits = 0 means "automatic". */
 size_t attn_fwd_workspace_size(int B, int H, int S_q, int S_k, int D, int num_splits);
 
-/* The split count attn_fwd would use (or attn_fwd_ex with num_splits), after
- * clamping; 1 means no split. Host-only, never touches the device. */
-int attn_fwd_num_splits(int B, int H, int S_q, int S_k, int D, int num_splits);
+/* The split count attn_fwd would use for these sizes and element type (or
+ * attn_fwd_ex with num_splits), after clamping; 1 means no split. The key
+ * tile, and so the clamping, depends on dtype (ATTN_F32: 32 keys;
+ * ATTN_F16 / ATTN_BF16: 128 keys at D = 64 / 128, 32 at D = 256); an unknown
+ * dtype or a non-positive size returns 1. Host-only, never touches the
+ * device. */
+int attn_fwd_num_splits(int B, int H, int S_q, int S_k, int D, int dtype, int num_splits);
 
 /*
  * attn_check_args -- the argument validation attn_fwd performs, without
@@ -283,7 +287,10 @@ int rope_hadamard_quant(const void* x, void* x8, float* scales, const signed cha
  * quant_per_tensor -- E4M3 quantization with one scale for the whole tensor
  * (four small launches on `stream`: clear, max |x|, quantize, final scale).
  * Used for V on the FP8 path and for the plain per-tensor FP8 baseline
- * without a transform.
+ * without a transform: the pages compare incoherent processing against FP8
+ * "without transformations" and report the error ratio ([NL] "3. Lage
+ * precisie (FP8) met reductie van kwantisatiefout"; [GN] "Niedrige
+ * FP8-Praezision und incoherent processing").
  *
  *   x       [B, H, S, D] in_dtype (ATTN_BF16 or ATTN_F16)
  *   x8      uint8 E4M3 codes (written), [B, H, S, D], or [B, H, D, S] when
@@ -304,10 +311,11 @@ int quant_per_tensor(const void* x, void* x8, float* scale, int B, int H, int S,
  *   q8, k8      [B, H, S_q|S_k, D] E4M3 codes
  *   q_scales    [B, H, ceil(S_q / block_rows)] float32 block scales of q8
  *   k_scales    [B, H, ceil(S_k / block_rows)] float32 block scales of k8
- *   v8          E4M3 codes of V, [B, H, S_k, D]; v_transposed must be 0 (the
- *               kernel transposes V in flight with ds_read_b64_tr_b8; the
- *               [B, H, D, S_k] form that quant_per_tensor can write is
- *               rejected with ATTN_ERR_UNSUPPORTED)
+ *   v8          E4M3 codes of V: [B, H, S_k, D] with v_transposed = 0 (the
+ *               kernel transposes V in flight), or [B, H, D, S_k] with
+ *               v_transposed = 1 (the layout quant_per_tensor writes with
+ *               write_transposed = 1; S_k must then be a multiple of 16,
+ *               else ATTN_ERR_UNSUPPORTED). Both give the same bits.
  *   v_scale     one device float32: the per-tensor scale of v8
  *   o           [B, H, S_q, D] bfloat16 (written); lse [B, H, S_q] float32
  *   block_rows  must be 64 (the key tile of the kernel)

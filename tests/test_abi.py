@@ -39,7 +39,7 @@ def test_binding_signatures_cover_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert attn.abi_version() == 1
+    assert attn.abi_version() == 2
     lib = attn.load()
     for code in (0, -1, -2, -3, -4, -5):
         assert lib.attn_status_string(code).decode() not in ("", "unknown status")
@@ -98,6 +98,10 @@ def test_split_plan():
     for n_req in (2, 3, 5, 7):
         assert attn.num_splits(1, 1, 4, 1000, 128, n_req) <= n_req
     assert attn.workspace_size(1, 1, 4, 640, 128, 1) == 0
+    # the float32 kernel's 32-key tile clamps a request differently from the 128-key bf16 tile
+    assert attn.num_splits(1, 1, 4, 300, 128, 5, dtype=attn.F32) == 5
+    assert attn.num_splits(1, 1, 4, 300, 128, 5, dtype=attn.BF16) == 3
+    assert attn.num_splits(1, 1, 4, 300, 128, 5, dtype=9) == 1
     n = attn.num_splits(64, 32, 1, 32768, 128)
     assert attn.workspace_size(64, 32, 1, 32768, 128) >= n * 64 * 32 * (128 + 1) * 4
 
@@ -195,3 +199,27 @@ def test_noalloc_refuses_splits_beyond_its_scratch():
     assert 0 < attn.workspace_size(64, 32, 1, 32768, 128) <= attn.NOALLOC_SCRATCH_BYTES
     hdr = open(HEADER).read()
     assert f"#define ATTN_NOALLOC_SCRATCH_BYTES (16u << 20)" in hdr and attn.NOALLOC_SCRATCH_BYTES == 16 << 20
+
+
+def fp8(**kw):
+    a = dict(q8=P, k8=P, v8=P, qs=P, ks=P, vs=P, o=P, lse=P, B=1, H=2, S_q=128, S_k=128, D=128, causal=0,
+             scale=0.125, br=64, vt=0)
+    a.update(kw)
+    return attn.load().attn_fwd_fp8(a["q8"], a["k8"], a["v8"], a["qs"], a["ks"], a["vs"], a["o"], a["lse"], a["B"],
+                                    a["H"], a["S_q"], a["S_k"], a["D"], a["causal"], ctypes.c_float(a["scale"]),
+                                    a["br"], a["vt"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(vs=None), attn.ERR_INVALID_ARG),
+    (dict(vt=2), attn.ERR_INVALID_ARG),
+    (dict(S_k=0), attn.ERR_INVALID_ARG),
+    (dict(D=64), attn.ERR_UNSUPPORTED),
+    (dict(br=32), attn.ERR_UNSUPPORTED),
+    (dict(causal=1, S_q=200, S_k=128), attn.ERR_UNSUPPORTED),
+    (dict(vt=1, S_k=100), attn.ERR_UNSUPPORTED),       # transposed V rows must be 16-byte aligned
+    (dict(k8=P + 8), attn.ERR_MISALIGNED),
+])
+def test_fp8_validation_rejects(kw, code):
+    """Host-side checks of attn_fwd_fp8 (including the transposed-V layout): refused before any launch."""
+    assert fp8(**kw) == code

@@ -301,3 +301,25 @@ def test_rope_hadamard_quant_fullsize_bitexact_and_zero_angles(gpu_lib):
     b8, bsc = gpu_lib.hadamard_quant(xg, sgg)
     torch.cuda.synchronize()
     assert torch.equal(a8, b8) and torch.equal(asc, bsc)
+
+
+@pytest.mark.parametrize("S_q,S_k,causal", [(520, 512, False), (300, 1008, True), (130, 48, False),
+                                            (2100, 2112, True)])
+def test_fp8_attention_transposed_v_same_bits(gpu_lib, S_q, S_k, causal):
+    """V given as [B, H, D, S_k] codes (quant_per_tensor's transposed output, v_transposed = 1) gives the
+    same O and LSE bits as the [B, H, S_k, D] codes: the same probabilities meet the same V values in the
+    same order of the P V product."""
+    note(f"fp8 transposed V S_q{S_q} S_k{S_k} causal={causal}")
+    B, H, D = 1, 2, 128
+    q, k, v = inputs.qkv(B, H, S_q, S_k, D, seed=23, dtype=torch.bfloat16, device="cuda", outliers=True)
+    sg = inputs.signs(D, 23).cuda()
+    q8, qs = gpu_lib.hadamard_quant(q, sg)
+    k8, ks = gpu_lib.hadamard_quant(k, sg)
+    v8, vs = gpu_lib.quant_per_tensor(v)
+    vt8, vts = gpu_lib.quant_per_tensor(v, transposed=True)
+    o1, l1 = gpu_lib.fwd_fp8(q8, k8, v8, qs, ks, vs, causal=causal, scale=1 / math.sqrt(D))
+    o2, l2 = gpu_lib.fwd_fp8(q8, k8, vt8, qs, ks, vts, causal=causal, scale=1 / math.sqrt(D), v_transposed=True)
+    torch.cuda.synchronize()
+    assert torch.equal(vs, vts) and torch.equal(vt8, v8.transpose(2, 3).contiguous())
+    assert bool(torch.isfinite(o2.float()).all())
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
