@@ -284,6 +284,8 @@ def main():
                                        "bwd_d64", "persistent"],
                     default=None,
                     help="run just this extra workload and print its JSON (for profiling one kernel family)")
+    ap.add_argument("--point", type=str, default=None, metavar="B,H,S_q,S_k,D,causal",
+                    help="run just this one bf16 forward workload through attn_fwd and print its JSON")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="instead of the bench, run K plain device-to-device copies of this many bytes "
                          "(reference for scaling memory-traffic counters)")
@@ -305,6 +307,11 @@ def main():
                           "gbps_read_plus_write": round(2 * args.copy_bytes / ms / 1e6, 1)}), flush=True)
         return
     attn.load()
+    if args.point is not None:
+        B, H, S_q, S_k, D, causal = (int(x) for x in args.point.split(","))
+        res = bf16_point(B, H, S_q, S_k, D, bool(causal), steps=args.steps, warmup=args.warmup)
+        print(json.dumps({"point": args.point, "result": res}), flush=True)
+        return
     if args.only is not None:
         st, wu = args.steps, args.warmup
         runs = {
