@@ -253,7 +253,10 @@ fwd_d256_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
         }
 
         // ---- online softmax (base 2, scale folded into c)
-        float mx[QB];
+        // a row's keys are split over the two halves of the wave: when
+        // neither half's maximum passes the bound, the row's does not either,
+        // so the exchange between the halves waits for a move
+        float xh[QB];
         bool grow = false;
   #pragma unroll
         for (int qb = 0; qb < QB; qb++) {
@@ -262,14 +265,13 @@ fwd_d256_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
           for (int kb = 0; kb < C::KB; kb++)
   #pragma unroll
             for (int e = 0; e < 16; e++) x = fmaxf(x, s[kb][qb][e]);
-          x = pair_max(x) * c;
-          mx[qb] = x;
-          grow |= x > m[qb] + kTau256;
+          xh[qb] = x;
+          grow |= x * c > m[qb] + kTau256;
         }
         if (__any(grow)) {
   #pragma unroll
           for (int qb = 0; qb < QB; qb++) {
-            const float mnew = fmaxf(m[qb], mx[qb]);
+            const float mnew = fmaxf(m[qb], pair_max(xh[qb]) * c);
             const float ref = mnew == kNegInf ? 0.0f : mnew;
             const float alpha = fast_exp2(m[qb] - ref);   // 0 when m was -inf
             m[qb] = mnew;

@@ -310,13 +310,16 @@ fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ K8, c
             if (!ok) s[kb][4 * i + jx] = kNegInf;
           }
     }
-    float x = kNegInf;
+    // the row's keys are split over the two halves of the wave: when neither
+    // half's maximum passes the bound, the row's does not either, so the
+    // exchange between the halves is needed only when the reference moves
+    float xh = kNegInf;
 #pragma unroll
     for (int kb = 0; kb < KB8; kb++)
 #pragma unroll
-      for (int e = 0; e < 16; e++) x = fmaxf(x, s[kb][e]);
-    x = pair_max(x) * cc;
-    if (__any(x > m + kTau8)) {
+      for (int e = 0; e < 16; e++) xh = fmaxf(xh, s[kb][e]);
+    if (__any(xh * cc > m + kTau8)) {
+      const float x = pair_max(xh) * cc;
       const float mnew = fmaxf(m, x);
       const float r = mnew == kNegInf ? 0.0f : mnew;
       const float alpha = fast_exp2(m - r);      // 0 when m was -inf

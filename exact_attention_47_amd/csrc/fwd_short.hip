@@ -290,14 +290,15 @@ fwd_short_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __re
 #pragma unroll
         for (int e = 0; e < 16; e++) o[db][e] *= alpha;
     };
-    auto row_max = [&]() {
+    auto half_max = [&]() {                  // this lane's half of the row
       float x = kNegInf;
 #pragma unroll
       for (int kb = 0; kb < C::KB; kb++)
 #pragma unroll
         for (int e = 0; e < 16; e++) x = fmaxf(x, s[kb][e]);
-      return pair_max(x) * c;
+      return x;
     };
+    auto row_max = [&]() { return pair_max(half_max()) * c; };
     if constexpr (D == 64) {
       // A lane's tile sum bounds each of its P, so the row maximum is
       // computed only when some sum exceeds 2^8 (or a row has no reference
@@ -317,9 +318,12 @@ fwd_short_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __re
       }
       l += ls;
     } else {
-      // the reference moves when a row's maximum exceeds it by more than 8
-      const float x = row_max();
-      if (__any(x > m + 8.0f)) move_reference(x);
+      // the reference moves when a row's maximum exceeds it by more than 8;
+      // the row's keys are split over the two halves of the wave, and when
+      // neither half's maximum passes the bound the row's does not either, so
+      // the exchange between the halves is needed only when it moves
+      const float xh = half_max();
+      if (__any(xh * c > m + 8.0f)) move_reference(pair_max(xh) * c);
       exps(l);
     }
     {
