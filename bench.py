@@ -5,7 +5,9 @@
 
 One step is one call of ``attn_fwd`` on the headline workload: bfloat16,
 B=2, H=16, S_q=S_k=8192, D=128, non-causal, inputs N(0,1) already resident in
-HBM. W untimed steps, then exactly K timed steps between two synchronisations.
+HBM. W untimed steps (continued until at least 50 ms of steps have run, so
+that the engine clock has settled; the JSON line reports how many ran), then
+exactly K timed steps between two synchronisations.
 FLOPs per step: 4*B*H*S_q*S_k*D (halved for causal workloads).
 
 Printed: ONE JSON line with the headline throughput, the roofline of the
@@ -64,6 +66,9 @@ def kernel_source_hash():
 def flops(B, H, S_q, S_k, D, causal):
     f = 4.0 * B * H * S_q * S_k * D
     return f / 2 if causal else f
+
+
+SETTLE_MS = 50.0   # least untimed load before a timed region: the engine clock settles in ~20 ms
 
 
 def time_launches(fn, steps, warmup, settle_ms=30.0):
@@ -277,7 +282,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=50,
-                    help="untimed steps first (about 50 ms at the default: the engine clock settles under load)")
+                    help="untimed steps first (at least this many, and at least 50 ms of them: the engine clock "
+                         "settles under load)")
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["fp8", "decode", "d256", "causal_sweep", "d64_sweep", "varlen", "bwd",
@@ -339,9 +345,16 @@ def main():
     def step():
         attn.fwd(q, k, v, causal, scale, out=o, lse=lse)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    # W untimed steps, continued until at least SETTLE_MS of them have run: the
+    # engine clock takes some milliseconds of load to settle (the first
+    # launches after idle ran up to 25 % slower), longer than a few steps last
+    warm_steps = 0
+    t_w = time.perf_counter()
+    while warm_steps < args.warmup or (time.perf_counter() - t_w) * 1e3 < SETTLE_MS:
+        for _ in range(max(1, min(args.warmup, 10))):
+            step()
+            warm_steps += 1
+        torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     torch.cuda.synchronize()
@@ -367,6 +380,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_steps_run": warm_steps,
         "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
