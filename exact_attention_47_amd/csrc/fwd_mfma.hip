@@ -137,8 +137,12 @@ fwd_mfma_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
     const int nbh = per_xcd ? BH >> 3 : BH;
     const long long i = (long long)it * gx + ((it & 1) ? gx - 1 - j : j);
     if (i >= (long long)nbh * n_qt) break;
-    const int level = (int)(i / nbh);
-    const int hsel = (int)(i % nbh);
+    // items by head, heaviest query tile first within a head: the workgroups
+    // of a round share one or two heads' K and V in L2, and when the tile
+    // count and the workgroups per XCD divide one another the snake pairs
+    // every tile with its mirror (level l with n_qt - 1 - l)
+    const int level = (int)(i % n_qt);
+    const int hsel = (int)(i / n_qt);
     bh = per_xcd ? x + 8 * hsel : hsel;
     qt = n_qt - 1 - level;
     split = 0;
