@@ -95,6 +95,24 @@ def time_launches(fn, steps, warmup, settle_ms=30.0):
     return sum(per) / len(per), min(per)
 
 
+def stream_ceiling(kind, iters):
+    """TFLOP/s the matrix cores sustain on a stream of one instruction (attn_mfma_stream; kind 0: the bf16
+    32x32x16 MFMA of the bf16 kernels, 1: the fp8 32x32x64 one of the FP8 kernel): one untimed launch
+    (50-100 ms, long enough for the clock to settle at the power limit), then the mean of two timed ones."""
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    sink = torch.empty(2 * n_cu * 256, dtype=torch.float32, device="cuda")
+    attn.mfma_stream(kind, iters, sink=sink)
+    rates = []
+    for _ in range(2):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        flop = attn.mfma_stream(kind, iters, sink=sink)
+        e1.record()
+        torch.cuda.synchronize()
+        rates.append(flop / (e0.elapsed_time(e1) * 1e-3) / 1e12)
+    return sum(rates) / len(rates)
+
+
 def bf16_point(B, H, S_q, S_k, D, causal, steps=10, warmup=3, seed=0, persistent=None):
     """One bf16 forward workload; persistent=n times attn_fwd_persistent on n workgroups (0 = one per CU)."""
     q, k, v = inputs.qkv(B, H, S_q, S_k, D, seed=seed, dtype=torch.bfloat16, device="cuda")
@@ -202,11 +220,13 @@ def fp8_point(steps=10, warmup=3):
     rope_ms, _ = time_launches(lambda: attn.rope_hadamard_quant(q, sg, cos, sin, mode=1, out=(q8, qs)),
                                steps, warmup)
     fl = flops(B, H, S, S, D, False)
+    ceil8 = stream_ceiling(1, 25000)
     pre_bytes = B * H * S * D * (2 + 1) + B * H * (S // 64) * 4
     vq_bytes = B * H * S * D * (2 + 2 + 1)
     e2e = 2 * pre_ms + vq_ms + att_ms
     res = {"B": B, "H": H, "S": S, "D": D, "attn_ms": round(att_ms, 4),
            "attn_tflops": round(fl / att_ms / 1e9, 1), "attn_pct_fp8_peak": round(100 * fl / att_ms / 1e9 / PEAK_FP8, 1),
+           "fp8_mfma_stream_tflops": round(ceil8, 1), "attn_frac_of_stream": round(fl / att_ms / 1e9 / ceil8, 4),
            "hadamard_quant_ms": round(pre_ms, 4), "hadamard_quant_gbps": round(pre_bytes / pre_ms / 1e6, 1),
            "rope_hadamard_quant_ms": round(rope_ms, 4),
            "rope_hadamard_quant_gbps": round(pre_bytes / rope_ms / 1e6, 1),
@@ -370,6 +390,7 @@ def main():
     fl = flops(B, H, S, S, D, causal)
     value = fl / (ms_per_step * 1e-3) / 1e12
     achieved = fl / (kern_ms * 1e-3) / 1e12
+    ceiling = stream_ceiling(0, 50000)
     del q, k, v, o, lse
     torch.cuda.empty_cache()
 
@@ -394,7 +415,12 @@ def main():
                      "frac": round(achieved / PEAK_BF16, 4),
                      "traffic": TRAFFIC_BYTES.get(kernel_source_hash()), "traffic_unit": "bytes per launch",
                      "kernel": "fwd_mfma_kernel<bf16, D=128, 128-key tiles, non-causal>",
-                     "kernel_ms": round(kern_ms, 4), "flop_per_launch": fl},
+                     "kernel_ms": round(kern_ms, 4), "flop_per_launch": fl,
+                     "ceiling": {"tflops": round(ceiling, 1), "frac": round(achieved / ceiling, 4),
+                                 "what": "attn_mfma_stream: v_mfma_f32_32x32x16_bf16 back to back on register "
+                                         "operands, two waves per SIMD on every CU, measured in this run (the "
+                                         "rate the matrix cores sustain once the clock settles at the power "
+                                         "limit)"}},
         "context": {"pages_h100_fa3_fp16_fwd_hdim128_seqlen8k_tflops": "640-660 (H100, not this machine)"},
     }
     if not args.no_extras:

@@ -47,6 +47,7 @@ _SIGS = {
     "attn_fwd_persistent": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i, _i, _vp]),
     "rope_hadamard_quant": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp]),
     "attn_bwd": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i, _vp]),
+    "attn_mfma_stream": (_i, [_i, _i, _vp, _sz, ctypes.POINTER(ctypes.c_double), _vp]),
 }
 
 
@@ -95,6 +96,24 @@ def _need_gpu(*ts):
 
 def abi_version() -> int:
     return load().attn_abi_version()
+
+
+def mfma_stream(kind: int, iters: int, sink=None, device=None) -> float:
+    """Enqueue ``attn_mfma_stream`` on the current stream; returns the launch's floating-point operations.
+
+    ``kind`` 0 is the bf16 32x32x16 instruction, 1 the fp8 32x32x64 one. ``sink`` (float32, one value per
+    thread: 2 * CUs * 256) is allocated when not given; time the call with events on the current stream.
+    """
+    dev = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
+    if sink is None:
+        n_cu = torch.cuda.get_device_properties(dev).multi_processor_count
+        sink = torch.empty(2 * n_cu * 256, dtype=torch.float32, device=dev)
+    _need_gpu(sink)
+    flop = ctypes.c_double(0.0)
+    _check("attn_mfma_stream", load().attn_mfma_stream(int(kind), int(iters), _ptr(sink),
+                                                       sink.numel() * sink.element_size(), ctypes.byref(flop),
+                                                       _stream(sink.device)))
+    return float(flop.value)
 
 
 def workspace_size(B, H, S_q, S_k, D, num_splits=0) -> int:

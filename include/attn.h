@@ -32,7 +32,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 2
+#define ATTN_ABI_VERSION 3
 
 /* element types */
 #define ATTN_F32  0
@@ -329,6 +329,30 @@ int attn_fwd_fp8(const void* q8, const void* k8, const void* v8,
                  const float* q_scales, const float* k_scales, const float* v_scale,
                  void* o, float* lse, int B, int H, int S_q, int S_k, int D,
                  int causal, float scale, int block_rows, int v_transposed, void* stream);
+
+/*
+ * attn_mfma_stream -- a measurement aid for the roofline report, outside the
+ * attention path. The data-sheet peaks assume the top engine clock; under a
+ * long stream of matrix instructions the socket reaches its power limit and
+ * the clock settles lower. This call enqueues one kernel that runs
+ * back-to-back matrix instructions of one kind on register operands on every
+ * compute unit (two waves per SIMD, 32 * iters instructions per wave, eight
+ * operand fragments in rotation, no memory traffic but one float per thread
+ * to `sink`), so that the rate the matrix cores sustain can be stated beside
+ * the peak. Time it with events around the call, after a warm-up launch.
+ *   kind        0: v_mfma_f32_32x32x16_bf16 (the instruction of the bf16 /
+ *               fp16 attention kernels); 1: v_mfma_scale_f32_32x32x64_f8f6f4
+ *               on E4M3 codes with unit scales (that of attn_fwd_fp8)
+ *   iters       iterations per wave, > 0 (50000 runs for about 60 ms at kind 0)
+ *   sink        device buffer of float, 16-byte aligned, that receives one
+ *               value per thread: 2 * (compute units) * 256 floats
+ *   sink_bytes  its size in bytes
+ *   flop        host pointer; receives the floating-point operations the
+ *               launch performs (2 * M * N * K per instruction)
+ * Errors: ATTN_ERR_INVALID_ARG (unknown kind, iters <= 0, null pointer, sink
+ * smaller than needed), ATTN_ERR_MISALIGNED, ATTN_ERR_LAUNCH.
+ */
+int attn_mfma_stream(int kind, int iters, float* sink, size_t sink_bytes, double* flop, void* stream);
 
 #ifdef __cplusplus
 }

@@ -39,7 +39,7 @@ def test_binding_signatures_cover_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert attn.abi_version() == 2
+    assert attn.abi_version() == 3
     lib = attn.load()
     for code in (0, -1, -2, -3, -4, -5):
         assert lib.attn_status_string(code).decode() not in ("", "unknown status")
@@ -223,3 +223,16 @@ def fp8(**kw):
 def test_fp8_validation_rejects(kw, code):
     """Host-side checks of attn_fwd_fp8 (including the transposed-V layout): refused before any launch."""
     assert fp8(**kw) == code
+
+
+def test_mfma_stream_rejects_bad_arguments_on_the_host():
+    """attn_mfma_stream checks its arguments before it asks for the device (nothing is dereferenced)."""
+    lib = attn.load()
+    P = ctypes.c_void_p(4096)
+    f = ctypes.c_double(0.0)
+    assert lib.attn_mfma_stream(2, 10, P, 1 << 20, ctypes.byref(f), None) == attn.ERR_INVALID_ARG
+    assert lib.attn_mfma_stream(-1, 10, P, 1 << 20, ctypes.byref(f), None) == attn.ERR_INVALID_ARG
+    assert lib.attn_mfma_stream(0, 0, P, 1 << 20, ctypes.byref(f), None) == attn.ERR_INVALID_ARG
+    assert lib.attn_mfma_stream(0, 10, None, 1 << 20, ctypes.byref(f), None) == attn.ERR_INVALID_ARG
+    assert lib.attn_mfma_stream(0, 10, P, 1 << 20, None, None) == attn.ERR_INVALID_ARG
+    assert lib.attn_mfma_stream(1, 10, ctypes.c_void_p(4100), 1 << 20, ctypes.byref(f), None) == attn.ERR_MISALIGNED
