@@ -101,8 +101,9 @@ def abi_version() -> int:
 def mfma_stream(kind: int, iters: int, sink=None, device=None) -> float:
     """Enqueue ``attn_mfma_stream`` on the current stream; returns the launch's floating-point operations.
 
-    ``kind`` 0 is the bf16 32x32x16 instruction, 1 the fp8 32x32x64 one. ``sink`` (float32, one value per
-    thread: 2 * CUs * 256) is allocated when not given; time the call with events on the current stream.
+    ``kind`` 0 is the bf16 32x32x16 instruction, 1 the fp8 32x32x64 one, 2 the bf16 16x16x32 one. ``sink``
+    (float32, one value per thread: 2 * CUs * 256) is allocated when not given; time the call with events on
+    the current stream.
     """
     dev = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
     if sink is None:

@@ -193,13 +193,13 @@ extern "C" {
 int attn_abi_version(void) { return ATTN_ABI_VERSION; }
 
 int attn_mfma_stream(int kind, int iters, float* sink, size_t sink_bytes, double* flop, void* stream) {
-  if ((kind != 0 && kind != 1) || iters <= 0 || sink == nullptr || flop == nullptr) return ATTN_ERR_INVALID_ARG;
+  if (kind < 0 || kind > 2 || iters <= 0 || sink == nullptr || flop == nullptr) return ATTN_ERR_INVALID_ARG;
   if (!aligned(sink, 16)) return ATTN_ERR_MISALIGNED;
   const int n_cu = cu_count();
   if (n_cu <= 0) return ATTN_ERR_LAUNCH;
   const long long blocks = 2LL * n_cu;   // four waves each: two waves per SIMD on every CU
   if ((long long)sink_bytes < blocks * 256 * (long long)sizeof(float)) return ATTN_ERR_INVALID_ARG;
-  const double per_instr = kind == 0 ? 2.0 * 32 * 32 * 16 : 2.0 * 32 * 32 * 64;
+  const double per_instr = kind == 0 ? 2.0 * 32 * 32 * 16 : kind == 1 ? 2.0 * 32 * 32 * 64 : 2.0 * 16 * 16 * 32;
   *flop = per_instr * 32.0 * (double)iters * (double)(blocks * 4);
   if (attn::launch_mfma_stream(kind, iters, sink, (int)blocks, (hipStream_t)stream) != hipSuccess) {
     say("attn_mfma_stream", ATTN_ERR_LAUNCH);

@@ -43,11 +43,39 @@ __device__ __forceinline__ v8i frag_e4m3(uint32_t seed) {
   return f;
 }
 
-// KIND 0: v_mfma_f32_32x32x16_bf16; 1: v_mfma_scale_f32_32x32x64_f8f6f4 (E4M3, unit scales).
-// Per iteration and wave: 32 instructions (four accumulators, eight fragments).
+// KIND 0: v_mfma_f32_32x32x16_bf16; 1: v_mfma_scale_f32_32x32x64_f8f6f4 (E4M3, unit scales);
+// 2: v_mfma_f32_16x16x32_bf16. Per iteration and wave: 32 instructions (four
+// accumulators, eight fragments).
 template <int KIND>
 __global__ void __launch_bounds__(256) mfma_stream_kernel(float* __restrict__ sink, int iters) {
   const uint32_t tid = blockIdx.x * blockDim.x + threadIdx.x;
+  if constexpr (KIND == 2) {
+    v4f acc[4];
+#pragma unroll
+    for (int a = 0; a < 4; a++)
+#pragma unroll
+      for (int e = 0; e < 4; e++) acc[a][e] = 0.0f;
+    v8bf16 x[8], y[8];
+#pragma unroll
+    for (int u = 0; u < 8; u++) {
+      x[u] = frag_bf16(tid * 16 + u);
+      y[u] = frag_bf16(tid * 16 + 8 + u + 0x9e3779b9u);
+    }
+    for (int it = 0; it < iters; it++) {
+#pragma unroll
+      for (int u = 0; u < 8; u++)
+#pragma unroll
+        for (int a = 0; a < 4; a++)
+          acc[a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x[u], y[(u + a) & 7], acc[a], 0, 0, 0);
+    }
+    float s = 0.0f;
+#pragma unroll
+    for (int a = 0; a < 4; a++)
+#pragma unroll
+      for (int e = 0; e < 4; e++) s += acc[a][e];
+    sink[tid] = s;
+    return;
+  }
   v16f acc[4];
 #pragma unroll
   for (int a = 0; a < 4; a++)
@@ -96,8 +124,10 @@ __global__ void __launch_bounds__(256) mfma_stream_kernel(float* __restrict__ si
 hipError_t launch_mfma_stream(int kind, int iters, float* sink, int blocks, hipStream_t st) {
   if (kind == 0)
     hipLaunchKernelGGL(mfma_stream_kernel<0>, dim3((unsigned)blocks), dim3(256), 0, st, sink, iters);
-  else
+  else if (kind == 1)
     hipLaunchKernelGGL(mfma_stream_kernel<1>, dim3((unsigned)blocks), dim3(256), 0, st, sink, iters);
+  else
+    hipLaunchKernelGGL(mfma_stream_kernel<2>, dim3((unsigned)blocks), dim3(256), 0, st, sink, iters);
   return hipGetLastError();
 }
 

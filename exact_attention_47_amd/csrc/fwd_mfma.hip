@@ -1,4 +1,5 @@
-// Fused exact attention forward pass on gfx950 matrix cores (bf16 / fp16).
+// Fused exact attention forward pass on gfx950 matrix cores (bf16 / fp16,
+// D = 64 / 128).
 //
 // What is computed: O = softmax(scale * Q K^T [+ causal mask]) V and the row
 // logsumexp, block by block with online softmax rescaling, so the score matrix
@@ -9,7 +10,7 @@
 //
 // * Work split. One workgroup of 8 waves per (b, h, 256 query rows); each wave
 //   owns 32 query rows for the whole key loop and holds Q^T in registers. Keys
-//   are processed in tiles of BN.
+//   are processed in tiles of 128.
 //
 // * Ping-pong ([GN] "Pingpong-Scheduling zwischen Warpgroups"). Waves w and
 //   w+4 share a SIMD. Waves 0-3 (group 0) and 4-7 (group 1) run the same
@@ -26,13 +27,25 @@
 //   LDS, no registers) at the start of the step that reads stage t, and
 //   waited for just before the step's closing barrier.
 //
-// * Both GEMMs are transposed so that one lane owns one query row:
-//   S^T = K Q^T with v_mfma_f32_32x32x16 (A = K rows from LDS, B = Q^T from
-//   VGPRs): lane (h, n) holds 16 keys of query n, so row max and row sum need
-//   one exchange with lane n+32 only. O^T = V^T P^T (A = V^T read with
-//   ds_read_b64_tr_b16, which transposes in flight; B = P^T, which is the S^T
-//   accumulator after exp2 and conversion, already in the B operand's k order
-//   given the matching choice of keys for V^T).
+// * Both products run on v_mfma_f32_16x16x32 (16 cycles for a 16 x 16 x 32
+//   block; under the chip's power limit the matrix cores sustain it at a
+//   higher rate than the 32x32x16 form, which this kernel used before:
+//   +3 to +7 % on the same schedule). Both are transposed so that a lane
+//   owns query rows:
+//   - S^T = K Q^T per 16-key block kb and 16-query block qb (A = 16 keys x 32
+//     d from LDS, B = Q^T from registers). Lane (g = lane / 16, n = lane %
+//     16) holds keys kb*16 + 4g + i (i < 4) of query qb*16 + n: a lane owns
+//     two query rows (qb = 0, 1) with 32 scores each per tile. Each K
+//     fragment serves both query blocks, so the LDS bytes per product are
+//     those of a 32-row block.
+//   - O^T += V^T P^T per 32-key pair p of S blocks (2p, 2p+1) and 16-wide d
+//     block: the B operand's eight k rows of lane (g, n) are the lane's four
+//     keys of block 2p then its four of block 2p+1, i.e. the lane's S values
+//     of that pair after exp2 and conversion. The A operand takes the same
+//     key order: two ds_read_b64_tr_b16 per fragment (rows 32p + 4g + r and
+//     32p + 16 + 4g + r), which transpose 4 x 16 blocks in flight.
+//   - Row maxima (rare) and the final row sums reduce over the four lanes of
+//     a query: one exchange 16 lanes away, one 32 lanes away.
 //
 // * Softmax in base 2 with the scale folded in: p = 2^(s * c - m), c =
 //   scale * log2(e). The reference m moves only when a lane's sum of P over
@@ -41,43 +54,46 @@
 //   nor a rescale of O, and the result is still exact because the final
 //   O / l and LSE use the same m.
 //
-// * LDS layout. Tiles are stored unpadded ([BN][D]) with a 16-byte-chunk XOR
-//   swizzle that depends on the row, so that the K reads (16 lanes per LDS
-//   cycle: 16 rows, one chunk each) and the transposed V reads (32 lanes per
-//   cycle: 4 rows x 64 bytes) each touch all 64 banks once. The direct loads
-//   write 1 KiB per wave instruction, lane i at byte 16*i; each lane fetches
-//   the global chunk that the swizzle places there.
+// * LDS layout. Tiles are stored unpadded ([128][D]) with a 16-byte-chunk
+//   XOR swizzle that depends on the row, so that a K fragment read (16 rows,
+//   one chunk each per LDS cycle) and a transposed V read (8 rows, one
+//   32-byte segment each per LDS cycle) each touch all 64 banks once. The
+//   direct loads write 1 KiB per wave instruction, lane i at byte 16*i; each
+//   lane fetches the global chunk that the swizzle places there.
 #include "common.h"
 #include "kernels.h"
 
 namespace attn {
+namespace {
 
 template <typename T> struct Mma;
 template <> struct Mma<__bf16> {
   typedef v8bf16 frag;
-  static __device__ __forceinline__ v16f mma(frag a, frag b, v16f c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  static __device__ __forceinline__ v4f mma(frag a, frag b, v4f c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
   }
   static __device__ __forceinline__ frag cvt(v8f x) { return __builtin_convertvector(x, v8bf16); }
 };
 template <> struct Mma<_Float16> {
   typedef v8f16 frag;
-  static __device__ __forceinline__ v16f mma(frag a, frag b, v16f c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  static __device__ __forceinline__ v4f mma(frag a, frag b, v4f c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
   }
   static __device__ __forceinline__ frag cvt(v8f x) { return __builtin_convertvector(x, v8f16); }
 };
 
-template <int D, int BN_>
+template <int D_>
 struct FwdCfg {
+  static constexpr int D = D_;
   static constexpr int NW = 8;                  // waves per workgroup (two groups of 4)
   static constexpr int NT = NW * 64;
   static constexpr int BM = NW * 32;            // query rows per workgroup
-  static constexpr int BN = BN_;                // keys per tile
-  static constexpr int KB = BN / 32;            // 32-key blocks per tile
-  static constexpr int DS = D / 16;             // k-steps of the S^T product
-  static constexpr int DB = D / 32;             // 32-wide column blocks of O^T
-  static constexpr int RB = 2 * D;              // bytes per K/V row
+  static constexpr int BN = 128;                // keys per tile
+  static constexpr int KB = BN / 16;            // 16-key blocks of S^T
+  static constexpr int KP = BN / 32;            // 32-key steps of O^T
+  static constexpr int DS = D / 32;             // k-steps of S^T
+  static constexpr int DB = D / 16;             // 16-wide column blocks of O^T
+  static constexpr int RB = 2 * D;              // bytes per K/V row in LDS
   static constexpr int TILE = BN * RB;          // bytes per K or V tile
   static constexpr int STAGE = 2 * TILE;        // K(t) then V(t-1)
   static constexpr int LDS = 2 * STAGE;
@@ -86,49 +102,62 @@ struct FwdCfg {
   static_assert(TILE % (NT * 16) == 0, "tile must split evenly into 1 KiB wave loads");
 };
 
-// Row-dependent 16-byte-chunk XOR swizzles of the K and V tiles.
+// Row-dependent 16-byte-chunk XOR swizzles. A K fragment read serves 16 rows
+// with one chunk each per LDS cycle; a transposed V read 8 rows with one
+// 32-byte segment each. With 256-byte rows (D = 128) every row starts on bank
+// 0; with 128-byte rows (D = 64) odd rows start on bank 32, so the swizzle
+// takes the row bits above the lowest.
 template <int D> __device__ __forceinline__ int k_swz(int r) { return D == 64 ? (r >> 1) & 7 : r & 15; }
-template <int D> __device__ __forceinline__ int v_swz(int r) { return D == 64 ? 4 * ((r >> 1) & 1) : 4 * (r & 3); }
+template <int D> __device__ __forceinline__ int v_swz(int r) { return D == 64 ? 2 * ((r >> 1) & 3) : 2 * (r & 7); }
 
-constexpr float kSumMax = 256.0f;   // lazy rescale: a lane's tile sum of P may reach 2^8
-constexpr int kVmcnt0 = 0x0070 | 0x0F00;   // s_waitcnt vmcnt(0), other counters unconstrained
+constexpr float kSumMax = 256.0f;        // lazy rescale: a lane's tile sum of P may reach 2^8
+constexpr int kVmcnt0 = 0x0070 | 0x0F00;  // s_waitcnt vmcnt(0), other counters unconstrained
 
-template <typename T, int D, int BN, bool CAUSAL, bool SPLIT, bool VARLEN, bool PERSIST>
+// maximum / sum over the four lanes n, n+16, n+32, n+48 of a query
+__device__ __forceinline__ float quad_max(float x) { return pair_max(fmaxf(x, __shfl_xor(x, 16))); }
+__device__ __forceinline__ float quad_sum(float x) { return pair_sum(x + __shfl_xor(x, 16)); }
+
+template <typename T, int D, bool CAUSAL, bool SPLIT, bool VARLEN, bool PERSIST>
 __global__ void __launch_bounds__(512)
 __attribute__((amdgpu_waves_per_eu(2, 2)))
 fwd_mfma_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
-                T* __restrict__ O, float* __restrict__ LSE,
-                float* __restrict__ Opart, float* __restrict__ Lpart,
-                int BH, int S_q_, int S_k_, int n_qt, int n_split, int keys_per_split, float c,
-                const int* __restrict__ cu_q, const int* __restrict__ cu_k, int H, int total_q)
+                  T* __restrict__ O, float* __restrict__ LSE,
+                  float* __restrict__ Opart, float* __restrict__ Lpart,
+                  int BH, int S_q_, int S_k_, int n_qt, int n_split, int keys_per_split, float c,
+                  const int* __restrict__ cu_q, const int* __restrict__ cu_k, int H, int total_q)
 {
   static_assert(!(VARLEN && SPLIT), "packed batches run unsplit");
   static_assert(!(PERSIST && (VARLEN || SPLIT)), "the persistent grid runs dense, unsplit work");
-  using C = FwdCfg<D, BN>;
+  using C = FwdCfg<D>;
   using M = Mma<T>;
   typedef typename M::frag frag;
   __shared__ __attribute__((aligned(1024))) char lds[C::LDS];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int grp = wave >> 2;       // ping-pong group
-  const int hh = lane >> 5;        // lane half
-  const int nn = lane & 31;        // query column owned by this lane
 
   // A persistent grid (PERSIST) runs this body once per work item it is
   // dealt; otherwise there is one workgroup per item and one pass.
   for (int it = 0;; it++) {
+  // (per item, the lane index passes through an empty asm statement so that
+  // no lane-dependent value is hoisted out of the item loop, where it would
+  // hold a register across every item)
+  int lane = tid & 63;
+  if (PERSIST) asm volatile("" : "+v"(lane));
+  const int g = lane >> 4;         // 16-lane group: rows 4g..4g+3 of each 16 x 16 output block
+  const int n = lane & 15;         // query column within a 16-query block
   // ---- which (b*h, q tile, split) this workgroup computes
   int split, qt, bh;
   if (PERSIST) {
     // Fixed grid of G workgroups (at most one per CU, all resident). The
     // items, heaviest query tiles first, are dealt in a snake: on even
     // rounds workgroup j takes the j-th item of the round, on odd rounds the
-    // (G-1-j)-th, so the heavy and light causal tiles pair up and every
-    // workgroup gets about the same number of keys. When B*H and G are
-    // multiples of 8 the deal runs per XCD (workgroup g sits on XCD g % 8)
-    // over the heads of that XCD only, so a head's tiles share one L2.
+    // (G-1-j)-th, so heavy and light causal tiles pair up. When B*H and G
+    // are multiples of 8 the deal runs per XCD (workgroup g sits on XCD
+    // g % 8) over that XCD's heads, and within an XCD by head, heaviest
+    // query tile first: the workgroups of a round share one or two heads'
+    // K and V in L2.
     const int G = gridDim.x;
     const bool per_xcd = (BH & 7) == 0 && (G & 7) == 0;
     const int x = per_xcd ? blockIdx.x & 7 : 0;
@@ -137,16 +166,13 @@ fwd_mfma_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
     const int nbh = per_xcd ? BH >> 3 : BH;
     const long long i = (long long)it * gx + ((it & 1) ? gx - 1 - j : j);
     if (i >= (long long)nbh * n_qt) break;
-    // items by head, heaviest query tile first within a head: the workgroups
-    // of a round share one or two heads' K and V in L2, and when the tile
-    // count and the workgroups per XCD divide one another the snake pairs
-    // every tile with its mirror (level l with n_qt - 1 - l)
     const int level = (int)(i % n_qt);
     const int hsel = (int)(i / n_qt);
     bh = per_xcd ? x + 8 * hsel : hsel;
     qt = n_qt - 1 - level;
     split = 0;
   } else if (!VARLEN && (SPLIT || !CAUSAL)) {
+    // equal work per item: contiguous shares of the items per XCD
     const int n_work = BH * n_qt * n_split;
     int work = xcd_swizzle(blockIdx.x, n_work);
     split = work % n_split;
@@ -155,21 +181,14 @@ fwd_mfma_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
     bh = work / n_qt;
     if (CAUSAL) qt = n_qt - 1 - qt;  // heaviest query tiles first
   } else {
-    // Packed batches and unsplit causal work: the workgroups' loads differ,
-    // so a contiguous share of the work per XCD (as above) would leave some
-    // XCDs with all the long sequences (packed) or all the late query tiles.
-    // Query tiles go out in descending order instead, all (b, h) at a time:
-    // high tiles exist only in long sequences, and causal tiles grow with the
-    // index, so the heaviest work starts first; the hardware deals
-    // consecutive workgroups to the 8 XCDs in turn, so (b, h) lands on XCD
-    // bh % 8 for every tile when B*H is a multiple of 8 (its K and V stay in
-    // one L2). Measured on causal D=128 8K: +2.5 % over the contiguous shares.
+    // Packed batches and unsplit causal work: query tiles in descending
+    // order (the heaviest work first), and (b, h) on XCD bh % 8 for every
+    // tile when B*H is a multiple of 8 (the hardware deals consecutive
+    // workgroups to the 8 XCDs in turn), so its K and V stay in one L2.
     split = 0;
     if (VARLEN && BH % 8 == 0) {
-      // packed: XCD x (workgroups x, x+8, ...) takes heads bh = x, x+8, ...,
-      // one at a time with all their query tiles (highest first): every XCD
-      // gets the same share of each sequence, and the tiles of one head run
-      // together, so its K and V are read from L2 rather than once per tile
+      // packed: XCD x takes heads x, x+8, ..., one at a time with all
+      // their query tiles (highest first)
       const int x = blockIdx.x % 8, j = blockIdx.x / 8;
       bh = x + 8 * (j / n_qt);
       qt = n_qt - 1 - j % n_qt;
@@ -220,39 +239,34 @@ fwd_mfma_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
   if (CAUSAL) k_end = min(k_end, q0 + C::BM - 1 + diag + 1);
   const int n_tiles = k_end > k_lo ? (k_end - k_lo + C::BN - 1) / C::BN : 0;
 
-
-  // ---- Q^T fragments (B operand of S^T), kept in registers
-  frag qf[C::DS];
-  {
-    const int q = wr0 + nn;
+  // ---- Q^T fragments (B operand of S^T): 8 d of query qb*16 + n, kept in registers
+  frag qf[C::DS][2];
+#pragma unroll
+  for (int qb = 0; qb < 2; qb++) {
+    const int q = wr0 + qb * 16 + n;
 #pragma unroll
     for (int ds = 0; ds < C::DS; ds++) {
       if (q < S_q) {
-        qf[ds] = *(const frag*)(Qh + (size_t)q * pitch + ds * 16 + 8 * hh);
+        qf[ds][qb] = *(const frag*)(Qh + (size_t)q * pitch + ds * 32 + 8 * g);
       } else {
 #pragma unroll
-        for (int e = 0; e < 8; e++) qf[ds][e] = (T)0.0f;
+        for (int e = 0; e < 8; e++) qf[ds][qb][e] = (T)0.0f;
       }
     }
   }
 
-  // ---- direct global -> LDS loads, issued by the 256 threads of group 0:
-  // stage s = K(s) (if s < n_tiles) and V(s-1) (if s >= 1) into buffer s & 1.
-  // Each wave instruction fills 1 KiB (RPI rows); lane i lands at byte 16*i
-  // and fetches the logical chunk the swizzle stores there. The loads are
-  // buffer loads on per-head resources. The rows a lane loads step by 16
-  // (D=128) or 32 (D=64) between its instructions, which leaves both swizzles
-  // unchanged, so its part of the offset is one constant and the rest (tile
-  // row and 1 KiB block) is wave-uniform: no vector arithmetic per load.
-  // The buffer range check covers the per-lane offset and not the scalar
-  // one, so that split serves only tiles that lie wholly inside K and V. A
-  // tile that reaches past the last row gets one resource per load
-  // instruction instead, built in scalar registers: its base is the
-  // instruction's first row and its range the bytes left after it, so the
-  // per-lane offset alone is checked and the rows past the end read zeros
-  // (their scores are masked, and zero V rows keep 0 * V finite whatever
-  // memory follows).
-  // (packed rows are strided: the range ends after the last row's D elements)
+  // ---- direct global -> LDS loads by the 256 threads of group 0: stage s =
+  // K(s) (if s < n_tiles) and V(s-1) (if s >= 1) into buffer s & 1. Each wave
+  // instruction fills 1 KiB (RPI rows); lane i lands at byte 16*i and fetches
+  // the logical chunk the swizzle stores there. A lane's rows step by 16
+  // (D = 128) or 32 (D = 64) between its instructions, which leaves both
+  // swizzles unchanged, so its part of the offset is one constant and the
+  // rest is wave-uniform. Tiles wholly inside K and V use the per-head buffer
+  // resources (whose range check covers the per-lane offset only); a tile
+  // reaching past the last row gets one resource per instruction, based at
+  // the instruction's first row with the bytes left after it as its range,
+  // so the rows past the end read zeros (their scores are masked, and zero V
+  // rows keep 0 * V finite whatever memory follows).
   const int kv_bytes = VARLEN ? (S_k > 0 ? (S_k - 1) * RBg + C::RB : 0) : S_k * C::RB;
   const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)Kh, (short)0, kv_bytes, 0x00020000);
   const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)Vh, (short)0, kv_bytes, 0x00020000);
@@ -260,12 +274,10 @@ fwd_mfma_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
   {
     const int rsub = (lane * 16) / C::RB;           // row within the wave instruction
     const int u = ((lane * 16) % C::RB) / 16;       // physical chunk within the row
-    const int r = wave * C::RPI + rsub;             // first row; later rows differ by a multiple of 16
+    const int r = wave * C::RPI + rsub;
     lane_k = rsub * RBg + ((u ^ k_swz<D>(r)) * 16);
     lane_v = rsub * RBg + ((u ^ v_swz<D>(r)) * 16);
   }
-  // (offsets and destinations go through locals: a target builtin with
-  // template-dependent argument expressions is dropped from the host pass)
   auto load_tile = [&](__amdgpu_buffer_rsrc_t rs, const T* head, int lane_off, int row0, char* tb) {
     if (row0 + C::BN <= S_k) {
 #pragma unroll
@@ -297,52 +309,48 @@ fwd_mfma_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
   };
 
   // ---- per-lane LDS read offsets (swizzle folded in)
-  // The XOR only reaches the low 3 (K) / 2 (V) bits of the chunk index, so
-  // the offsets repeat every 8 k-steps / 4 column blocks up to a constant.
-  constexpr int NKR = C::DS < 8 ? C::DS : 8;
-  constexpr int NVR = C::DB < 4 ? C::DB : 4;
-  const int xk = k_swz<D>(nn);                 // K row = kb*32 + nn: swizzle depends on nn only
-  int k_rd[NKR];
+  // K fragment (kb, ds): row kb*16 + n, logical chunk 4*ds + g.
+  int k_rd[C::DS];
 #pragma unroll
-  for (int ds = 0; ds < NKR; ds++) k_rd[ds] = nn * C::RB + (((2 * ds + hh) ^ xk) * 16);
-  const int g = lane >> 4, jj = lane & 15;
-  const int vrow = 4 * hh + (jj >> 2);         // V row = vrow + kb*32 + 16*ks + 8*part
-  const int xv = v_swz<D>(vrow);               // depends on vrow's low bits only
-  int v_rd[NVR];
+  for (int ds = 0; ds < C::DS; ds++) k_rd[ds] = n * C::RB + (((4 * ds + g) ^ k_swz<D>(n)) * 16);
+  // V fragment (p, db): lane n of group g addresses row 32p + 4g + n/4 (and
+  // 16 rows further for the second half), columns 16*db + 4*(n % 4) .. +3.
+  const int vrow = 4 * g + (n >> 2);
+  int v_rd[C::DB];
 #pragma unroll
-  for (int db = 0; db < NVR; db++)
-    v_rd[db] = vrow * C::RB + (((4 * db + 2 * (g & 1) + ((jj & 3) >> 1)) ^ xv) * 16) + 8 * (jj & 1);
+  for (int db = 0; db < C::DB; db++)
+    v_rd[db] = vrow * C::RB + (((2 * db + ((n & 3) >> 1)) ^ v_swz<D>(vrow)) * 16) + 8 * (n & 1);
 
-  v16f o[C::DB];
+  v4f o[C::DB][2];
 #pragma unroll
   for (int db = 0; db < C::DB; db++)
 #pragma unroll
-    for (int e = 0; e < 16; e++) o[db][e] = 0.0f;
-  v16f s[C::KB];
-  frag pf[C::KB][2];
-  float m = kNegInf, l = 0.0f;
+    for (int qb = 0; qb < 2; qb++)
+#pragma unroll
+      for (int e = 0; e < 4; e++) o[db][qb][e] = 0.0f;
+  v4f s[C::KB][2];
+  frag pf[C::KP][2];
+  float m[2] = {kNegInf, kNegInf}, l[2] = {0.0f, 0.0f};
 
   // causal: tiles that lie wholly after this wave's last row are skipped
   auto tile_active = [&](int t) { return !CAUSAL || k_lo + t * C::BN <= wr0 + 31 + diag; };
 
-  // matrix phase: O^T += V(t-1)^T P(t-1)^T, then S(t)^T = K(t) Q^T.
-  // Each product is a list of steps (one A fragment from LDS, one MFMA); the
-  // fragment of step j+LA is loaded while step j multiplies, and a scheduling
-  // barrier after every step keeps the compiler from hoisting further loads
-  // (which would cost registers the two waves per SIMD do not have).
+  // matrix phase: O^T += V(t-1)^T P(t-1)^T, then S(t)^T = K(t) Q^T. Each step
+  // loads one A fragment from LDS (LA steps ahead) and multiplies it into both
+  // query blocks; a scheduling barrier after every step keeps the compiler
+  // from hoisting further loads (registers the two waves per SIMD lack).
   constexpr int LA = 3;
-  constexpr int NPV = C::KB * 2 * C::DB;      // steps of O^T += V^T P^T
-  constexpr int NSK = C::DS * C::KB;          // steps of S^T = K Q^T
+  constexpr int NPV = C::KP * C::DB;
+  constexpr int NSK = C::DS * C::KB;
   auto gemm_phase = [&](int t) {
     const char* st = lds + (t & 1) * C::STAGE;
     if (t >= 1 && tile_active(t - 1)) {
       const char* vl = st + C::TILE;
       auto load = [&](int j) {
-        const int kb = j / (2 * C::DB), ks = (j / C::DB) % 2, db = j % C::DB;
-        const int off = (kb * 32 + 16 * ks) * C::RB;
-        const char* va = vl + v_rd[db % NVR] + (db / NVR) * 256 + off;
+        const int p = j / C::DB, db = j % C::DB;
+        const char* va = vl + v_rd[db] + p * 32 * C::RB;
         v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)va);
-        v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(va + 8 * C::RB));
+        v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(va + 16 * C::RB));
         return __builtin_bit_cast(frag, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       };
       frag ring[LA + 1];
@@ -351,15 +359,16 @@ fwd_mfma_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
 #pragma unroll
       for (int j = 0; j < NPV; j++) {
         if (j + LA < NPV) ring[(j + LA) % (LA + 1)] = load(j + LA);
-        const int kb = j / (2 * C::DB), ks = (j / C::DB) % 2, db = j % C::DB;
-        o[db] = M::mma(ring[j % (LA + 1)], pf[kb][ks], o[db]);
+        const int p = j / C::DB, db = j % C::DB;
+        o[db][0] = M::mma(ring[j % (LA + 1)], pf[p][0], o[db][0]);
+        o[db][1] = M::mma(ring[j % (LA + 1)], pf[p][1], o[db][1]);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
     if (t < n_tiles && tile_active(t)) {
       auto load = [&](int j) {
         const int ds = j / C::KB, kb = j % C::KB;
-        return *(const frag*)(st + k_rd[ds % NKR] + (ds / NKR) * 256 + kb * 32 * C::RB);
+        return *(const frag*)(st + k_rd[ds] + kb * 16 * C::RB);
       };
       frag ring[LA + 1];
 #pragma unroll
@@ -369,10 +378,12 @@ fwd_mfma_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
         if (j + LA < NSK) ring[(j + LA) % (LA + 1)] = load(j + LA);
         const int ds = j / C::KB, kb = j % C::KB;
         if (ds == 0) {
-          const v16f zero = {};
-          s[kb] = M::mma(ring[j % (LA + 1)], qf[ds], zero);
+          const v4f zero = {};
+          s[kb][0] = M::mma(ring[j % (LA + 1)], qf[ds][0], zero);
+          s[kb][1] = M::mma(ring[j % (LA + 1)], qf[ds][1], zero);
         } else {
-          s[kb] = M::mma(ring[j % (LA + 1)], qf[ds], s[kb]);
+          s[kb][0] = M::mma(ring[j % (LA + 1)], qf[ds][0], s[kb][0]);
+          s[kb][1] = M::mma(ring[j % (LA + 1)], qf[ds][1], s[kb][1]);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -385,76 +396,85 @@ fwd_mfma_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
     const int key0 = k_lo + t * C::BN;
     const bool need_mask = (key0 + C::BN > k_hi) || (CAUSAL && key0 + C::BN - 1 > wr0 + diag);
     if (need_mask) {
-      const int q = wr0 + nn;
+      // Key key0 + kb*16 + 4g + i is allowed iff kb*16 + i <= lim. The sign
+      // of the difference picks -inf or +inf as the bound of a minimum: two
+      // vector instructions per score and no lane masks (64 compares per
+      // tile would hold their 64-bit results in scalar registers).
 #pragma unroll
-      for (int kb = 0; kb < C::KB; kb++)
+      for (int qb = 0; qb < 2; qb++) {
+        const int last = CAUSAL ? min(k_hi - 1, wr0 + qb * 16 + n + diag) : k_hi - 1;
+        const int lim = last - key0 - 4 * g;
 #pragma unroll
-        for (int i = 0; i < 4; i++)
+        for (int kb = 0; kb < C::KB; kb++)
 #pragma unroll
-          for (int j = 0; j < 4; j++) {
-            const int key = key0 + kb * 32 + 8 * i + 4 * hh + j;
-            const bool ok = key < k_hi && (!CAUSAL || key <= q + diag);
-            if (!ok) s[kb][4 * i + j] = kNegInf;
+          for (int i = 0; i < 4; i++) {
+            const uint32_t sgn = (uint32_t)(lim - (kb * 16 + i)) & 0x80000000u;
+            s[kb][qb][i] = fminf(s[kb][qb][i], __builtin_bit_cast(float, sgn | 0x7f800000u));
           }
+      }
     }
-    // P = 2^(s*c - m) with the row's current reference m, summed in float32
-    // and converted to the matrix operand type.
-    auto exps = [&]() {
-      const float ref = m == kNegInf ? 0.0f : m;
-      float ls = 0.0f;
+    // P = 2^(s*c - m) per query row with its current reference, summed in
+    // float32 and converted to the matrix operand type (keys of block 2p,
+    // then of block 2p+1).
+    auto exps = [&](float* ls) {
 #pragma unroll
-      for (int kb = 0; kb < C::KB; kb++)
+      for (int qb = 0; qb < 2; qb++) {
+        const float ref = m[qb] == kNegInf ? 0.0f : m[qb];
+        float acc = 0.0f;
 #pragma unroll
-        for (int ks = 0; ks < 2; ks++) {
+        for (int p = 0; p < C::KP; p++) {
           v8f pv;
 #pragma unroll
           for (int e = 0; e < 8; e++) {
-            pv[e] = fast_exp2(__builtin_fmaf(s[kb][8 * ks + e], c, -ref));
-            ls += pv[e];
+            pv[e] = fast_exp2(__builtin_fmaf(s[2 * p + (e >> 2)][qb][e & 3], c, -ref));
+            acc += pv[e];
           }
-          pf[kb][ks] = M::cvt(pv);
+          pf[p][qb] = M::cvt(pv);
         }
-      return ls;
+        ls[qb] = acc;
+      }
     };
-    // The reference only has to keep every P <= 2^8. A lane's tile sum
-    // bounds each of its P, so the row maximum is computed only when some
-    // sum exceeds 2^8 (or a row has no reference yet): then m moves to
-    // the maximum, O and l are rescaled, and P is recomputed. Any reference
-    // reached this way gives the exact result, as the final O / l and LSE
-    // use the same m.
-    float ls = __builtin_inff();                 // forces the slow path below
-    if (!__any(m == kNegInf)) ls = exps();
-    if (__any(!(ls <= kSumMax))) {
-      float x = kNegInf;
+    // Only the sums are needed while every lane's tile sum of P stays within
+    // 2^8 (which bounds each P): the maximum is taken, O and l rescaled and P
+    // recomputed only when some sum exceeds it or a row has no reference
+    // yet. Any reference reached this way gives the exact result, as the
+    // final O / l and LSE use the same m.
+    float ls[2] = {__builtin_inff(), __builtin_inff()};
+    if (!__any(m[0] == kNegInf || m[1] == kNegInf)) exps(ls);
+    if (__any(!(ls[0] <= kSumMax) || !(ls[1] <= kSumMax))) {
 #pragma unroll
-      for (int kb = 0; kb < C::KB; kb++)
+      for (int qb = 0; qb < 2; qb++) {
+        float x = kNegInf;
 #pragma unroll
-        for (int e = 0; e < 16; e++) x = fmaxf(x, s[kb][e]);
-      x = pair_max(x) * c;
-      const float mnew = fmaxf(m, x);
-      const float ref = mnew == kNegInf ? 0.0f : mnew;
-      const float alpha = fast_exp2(m - ref);   // 0 when m was -inf, 1 when m stays
-      m = mnew;
-      l *= alpha;
+        for (int kb = 0; kb < C::KB; kb++)
 #pragma unroll
-      for (int db = 0; db < C::DB; db++)
+          for (int i = 0; i < 4; i++) x = fmaxf(x, s[kb][qb][i]);
+        x = quad_max(x) * c;
+        const float mnew = fmaxf(m[qb], x);
+        const float ref = mnew == kNegInf ? 0.0f : mnew;
+        const float alpha = fast_exp2(m[qb] - ref);   // 0 when m was -inf, 1 when m stays
+        m[qb] = mnew;
+        l[qb] *= alpha;
 #pragma unroll
-        for (int e = 0; e < 16; e++) o[db][e] *= alpha;
-      ls = exps();
+        for (int db = 0; db < C::DB; db++)
+#pragma unroll
+          for (int e = 0; e < 4; e++) o[db][qb][e] *= alpha;
+      }
+      exps(ls);
     }
-    l += ls;
+    l[0] += ls[0];
+    l[1] += ls[1];
   };
 
-  // Both groups run the same body, gemm(j) | barrier | softmax(j) | barrier;
-  // group 1 starts one barrier later and group 0 ends one barrier later, so
-  // group 1's matrix phase overlaps group 0's softmax and vice versa. Group 0
-  // fetches stage j+1 at the start of its softmax phase j and waits for it
-  // before that phase's closing barrier: both groups have finished reading
-  // stage j-1 (the buffer it overwrites) by then, stage j+1 is complete
-  // before either group reads it, and no LDS read is ever issued while a
-  // direct load is in flight (so the compiler adds no waits of its own).
-  // Inside the loop the barriers are bare s_barrier: the only memory that
-  // must be settled at a barrier is the staged tile, waited for explicitly.
+  // gemm(j) | barrier | softmax(j) | barrier, group 1 one barrier behind
+  // group 0, so each group's matrix phase overlaps the other's softmax.
+  // Group 0 fetches stage j+1 at the start of its softmax phase j and waits
+  // for it before that phase's closing barrier: both groups have finished
+  // reading stage j-1 (the buffer it overwrites) by then, stage j+1 is
+  // complete before either group reads it, and no LDS read is issued while
+  // a direct load is in flight. Inside the loop the barriers are bare
+  // s_barrier: the staged tile is the only memory to settle, waited for
+  // explicitly.
   auto barrier = [] {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
@@ -481,40 +501,39 @@ fwd_mfma_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
   }
 
   // ---- epilogue: normalise, logsumexp, store
-  const int q = wr0 + nn;
-  const float lt = pair_sum(l);
-  const bool has = m != kNegInf && lt > 0.0f;
-  const float inv = has ? 1.0f / lt : 0.0f;
-  const float lse = has ? (m + __builtin_log2f(lt)) * kLn2 : kNegInf;
-  if (q < S_q) {
-    if (!SPLIT) {
-      T* orow = Oh + (size_t)q * pitch;
 #pragma unroll
-      for (int db = 0; db < C::DB; db++)
+  for (int qb = 0; qb < 2; qb++) {
+    const int q = wr0 + qb * 16 + n;
+    const float lt = quad_sum(l[qb]);
+    const bool has = m[qb] != kNegInf && lt > 0.0f;
+    const float inv = has ? 1.0f / lt : 0.0f;
+    const float lse = has ? (m[qb] + __builtin_log2f(lt)) * kLn2 : kNegInf;
+    if (q < S_q) {
+      if (!SPLIT) {
+        T* orow = Oh + (size_t)q * pitch;
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
+        for (int db = 0; db < C::DB; db++) {
           typedef T v4t __attribute__((ext_vector_type(4)));
           v4t w;
 #pragma unroll
-          for (int j = 0; j < 4; j++) w[j] = (T)(o[db][4 * i + j] * inv);
-          *(v4t*)(orow + db * 32 + 8 * i + 4 * hh) = w;
+          for (int e = 0; e < 4; e++) w[e] = (T)(o[db][qb][e] * inv);
+          *(v4t*)(orow + db * 16 + 4 * g) = w;
         }
-      if (hh == 0) lseh[q] = lse;
-    } else {
-      const size_t prow = ((size_t)split * BH + bh) * S_q + q;
-      float* orow = Opart + prow * D;
+        if (g == 0) lseh[q] = lse;
+      } else {
+        const size_t prow = ((size_t)split * BH + bh) * S_q + q;
+        float* orow = Opart + prow * D;
 #pragma unroll
-      for (int db = 0; db < C::DB; db++)
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
+        for (int db = 0; db < C::DB; db++) {
           float4 w;
-          w.x = o[db][4 * i + 0] * inv;
-          w.y = o[db][4 * i + 1] * inv;
-          w.z = o[db][4 * i + 2] * inv;
-          w.w = o[db][4 * i + 3] * inv;
-          *(float4*)(orow + db * 32 + 8 * i + 4 * hh) = w;
+          w.x = o[db][qb][0] * inv;
+          w.y = o[db][qb][1] * inv;
+          w.z = o[db][qb][2] * inv;
+          w.w = o[db][qb][3] * inv;
+          *(float4*)(orow + db * 16 + 4 * g) = w;
         }
-      if (hh == 0) Lpart[prow] = lse;
+        if (g == 0) Lpart[prow] = lse;
+      }
     }
   }
   // Persistent: every wave has passed the loop's last barrier after its last
@@ -523,45 +542,30 @@ fwd_mfma_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
   }
 }
 
-// ---------------------------------------------------------------- launchers
-
-// Keys per tile for each head dimension (LDS: 2 stages x (K + V) tiles).
-#ifndef FWD_D64_BN
-#define FWD_D64_BN 128
-#endif
-#ifndef FWD_D128_BN
-#define FWD_D128_BN 128
-#endif
-
-template <int D> struct Shape;
-template <> struct Shape<64> { static constexpr int BN = FWD_D64_BN; };
-template <> struct Shape<128> { static constexpr int BN = FWD_D128_BN; };
-
 template <typename T, int D, bool CAUSAL, bool SPLIT, bool VARLEN = false, bool PERSIST = false>
-static hipError_t launch_one(const FwdArgs& a, hipStream_t st, int n_wg = 0) {
-  using C = FwdCfg<D, Shape<D>::BN>;
+hipError_t launch_one(const FwdArgs& a, hipStream_t st, int n_wg = 0) {
+  using C = FwdCfg<D>;
   // 32-bit buffer offsets (packed rows: S_k is the longest sequence's length)
   const long long row_bytes = VARLEN ? (long long)a.H * C::RB : C::RB;
   if ((long long)(a.S_k + C::BN) * row_bytes > 0x7fffffffLL) return hipErrorInvalidValue;
   const int n_qt = (a.S_q + C::BM - 1) / C::BM;
   const int n_work = a.B * a.H * n_qt * a.n_split;
   const int grid = PERSIST ? (n_wg < n_work ? n_wg : n_work) : n_work;
-  hipLaunchKernelGGL((fwd_mfma_kernel<T, D, Shape<D>::BN, CAUSAL, SPLIT, VARLEN, PERSIST>), dim3(grid), dim3(C::NT), 0,
-                     st, (const T*)a.q, (const T*)a.k, (const T*)a.v, (T*)a.o, a.lse, a.opart, a.lpart,
-                     a.B * a.H, a.S_q, a.S_k, n_qt, a.n_split, a.keys_per_split, a.c, a.cu_q, a.cu_k, a.H,
-                     a.total_q);
+  hipLaunchKernelGGL((fwd_mfma_kernel<T, D, CAUSAL, SPLIT, VARLEN, PERSIST>), dim3(grid), dim3(C::NT), 0, st,
+                     (const T*)a.q, (const T*)a.k, (const T*)a.v, (T*)a.o, a.lse, a.opart, a.lpart, a.B * a.H,
+                     a.S_q, a.S_k, n_qt, a.n_split, a.keys_per_split, a.c, a.cu_q, a.cu_k, a.H, a.total_q);
   return hipGetLastError();
 }
 
 template <typename T, int D>
-static hipError_t launch_d(const FwdArgs& a, hipStream_t st) {
+hipError_t launch_d(const FwdArgs& a, hipStream_t st) {
   const bool split = a.n_split > 1;
   if (a.causal) return split ? launch_one<T, D, true, true>(a, st) : launch_one<T, D, true, false>(a, st);
   return split ? launch_one<T, D, false, true>(a, st) : launch_one<T, D, false, false>(a, st);
 }
 
 template <typename T>
-static hipError_t launch_t(const FwdArgs& a, hipStream_t st) {
+hipError_t launch_t(const FwdArgs& a, hipStream_t st) {
   switch (a.D) {
     case 64: return launch_d<T, 64>(a, st);
     case 128: return launch_d<T, 128>(a, st);
@@ -569,13 +573,8 @@ static hipError_t launch_t(const FwdArgs& a, hipStream_t st) {
   return hipErrorInvalidValue;
 }
 
-int mfma_keys_per_tile(int D) {
-  return D == 64 ? Shape<64>::BN : D == 128 ? Shape<128>::BN : d256_keys_per_tile();
-}
-int mfma_rows_per_block(int D) { (void)D; return 256; }
-
 template <typename T>
-static hipError_t launch_varlen_t(const FwdArgs& a, hipStream_t st) {
+hipError_t launch_varlen_t(const FwdArgs& a, hipStream_t st) {
   switch (a.D) {
     case 64: return a.causal ? launch_one<T, 64, true, false, true>(a, st) : launch_one<T, 64, false, false, true>(a, st);
     case 128: return a.causal ? launch_one<T, 128, true, false, true>(a, st) : launch_one<T, 128, false, false, true>(a, st);
@@ -583,13 +582,8 @@ static hipError_t launch_varlen_t(const FwdArgs& a, hipStream_t st) {
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_fwd_varlen(const FwdArgs& a, hipStream_t st) {
-  if (a.dtype == 2) return launch_varlen_t<__bf16>(a, st);
-  return launch_varlen_t<_Float16>(a, st);
-}
-
 template <typename T>
-static hipError_t launch_persistent_t(const FwdArgs& a, int n_wg, hipStream_t st) {
+hipError_t launch_persistent_t(const FwdArgs& a, int n_wg, hipStream_t st) {
   switch (a.D) {
     case 64: return a.causal ? launch_one<T, 64, true, false, false, true>(a, st, n_wg)
                              : launch_one<T, 64, false, false, false, true>(a, st, n_wg);
@@ -599,16 +593,26 @@ static hipError_t launch_persistent_t(const FwdArgs& a, int n_wg, hipStream_t st
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_fwd_persistent(const FwdArgs& a, int n_wg, hipStream_t st) {
-  if (a.n_split != 1 || n_wg < 1) return hipErrorInvalidValue;
-  if (a.dtype == 2) return launch_persistent_t<__bf16>(a, n_wg, st);
-  return launch_persistent_t<_Float16>(a, n_wg, st);
-}
+}  // namespace
+
+int mfma_keys_per_tile(int D) { return D == 64 || D == 128 ? FwdCfg<128>::BN : d256_keys_per_tile(); }
+int mfma_rows_per_block(int D) { (void)D; return FwdCfg<128>::BM; }
 
 hipError_t launch_fwd_mfma(const FwdArgs& a, hipStream_t st) {
   if (a.D == 256) return launch_fwd_d256(a, st);
   if (a.dtype == 2) return launch_t<__bf16>(a, st);
   return launch_t<_Float16>(a, st);
+}
+
+hipError_t launch_fwd_varlen(const FwdArgs& a, hipStream_t st) {
+  if (a.dtype == 2) return launch_varlen_t<__bf16>(a, st);
+  return launch_varlen_t<_Float16>(a, st);
+}
+
+hipError_t launch_fwd_persistent(const FwdArgs& a, int n_wg, hipStream_t st) {
+  if (a.n_split != 1 || n_wg < 1) return hipErrorInvalidValue;
+  if (a.dtype == 2) return launch_persistent_t<__bf16>(a, n_wg, st);
+  return launch_persistent_t<_Float16>(a, n_wg, st);
 }
 
 }  // namespace attn

@@ -96,7 +96,8 @@ hipError_t launch_fwd_fp8(const void* q8, const void* k8, const void* v8, const 
                           hipStream_t st);
 
 // matrix-core stream for the roofline report (kind 0: bf16 32x32x16, 1: fp8
-// 32x32x64), `blocks` workgroups of four waves, one float per thread to sink
+// 32x32x64, 2: bf16 16x16x32), `blocks` workgroups of four waves, one float
+// per thread to sink
 hipError_t launch_mfma_stream(int kind, int iters, float* sink, int blocks, hipStream_t st);
 
 }  // namespace attn

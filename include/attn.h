@@ -32,7 +32,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 3
+#define ATTN_ABI_VERSION 4
 
 /* element types */
 #define ATTN_F32  0
@@ -340,10 +340,13 @@ int attn_fwd_fp8(const void* q8, const void* k8, const void* v8,
  * operand fragments in rotation, no memory traffic but one float per thread
  * to `sink`), so that the rate the matrix cores sustain can be stated beside
  * the peak. Time it with events around the call, after a warm-up launch.
- *   kind        0: v_mfma_f32_32x32x16_bf16 (the instruction of the bf16 /
- *               fp16 attention kernels); 1: v_mfma_scale_f32_32x32x64_f8f6f4
- *               on E4M3 codes with unit scales (that of attn_fwd_fp8)
- *   iters       iterations per wave, > 0 (50000 runs for about 60 ms at kind 0)
+ *   kind        0: v_mfma_f32_32x32x16_bf16 (that of the D = 256 forward,
+ *               short-range and backward kernels); 1:
+ *               v_mfma_scale_f32_32x32x64_f8f6f4 on E4M3 codes with unit
+ *               scales (that of attn_fwd_fp8); 2: v_mfma_f32_16x16x32_bf16
+ *               (that of the main D = 64 / 128 forward kernel)
+ *   iters       iterations per wave, > 0 (50000 runs for about 60 ms at kind 0,
+ *               about 30 ms at kind 2)
  *   sink        device buffer of float, 16-byte aligned, that receives one
  *               value per thread: 2 * (compute units) * 256 floats
  *   sink_bytes  its size in bytes

@@ -39,7 +39,7 @@ def test_binding_signatures_cover_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert attn.abi_version() == 3
+    assert attn.abi_version() == 4
     lib = attn.load()
     for code in (0, -1, -2, -3, -4, -5):
         assert lib.attn_status_string(code).decode() not in ("", "unknown status")
@@ -230,7 +230,7 @@ def test_mfma_stream_rejects_bad_arguments_on_the_host():
     lib = attn.load()
     P = ctypes.c_void_p(4096)
     f = ctypes.c_double(0.0)
-    assert lib.attn_mfma_stream(2, 10, P, 1 << 20, ctypes.byref(f), None) == attn.ERR_INVALID_ARG
+    assert lib.attn_mfma_stream(3, 10, P, 1 << 20, ctypes.byref(f), None) == attn.ERR_INVALID_ARG
     assert lib.attn_mfma_stream(-1, 10, P, 1 << 20, ctypes.byref(f), None) == attn.ERR_INVALID_ARG
     assert lib.attn_mfma_stream(0, 0, P, 1 << 20, ctypes.byref(f), None) == attn.ERR_INVALID_ARG
     assert lib.attn_mfma_stream(0, 10, None, 1 << 20, ctypes.byref(f), None) == attn.ERR_INVALID_ARG

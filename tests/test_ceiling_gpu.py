@@ -1,8 +1,8 @@
 """GPU check of attn_mfma_stream, the matrix-core stream that bench.py times beside the attention kernels.
 
-It is a measurement aid, not part of the attention path: the test checks that both kinds run, report the
+It is a measurement aid, not part of the attention path: the test checks that each kind runs, reports the
 floating-point operations the launch performs (2*M*N*K per instruction, 32*iters instructions per wave, two
-waves per SIMD on every CU), write one finite value per thread, and refuse a sink that is too small.
+waves per SIMD on every CU), writes one finite value per thread, and refuses a sink that is too small.
 """
 
 import pytest
@@ -13,7 +13,7 @@ from exact_attention_47_amd import attn
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("kind,mnk", [(0, 32 * 32 * 16), (1, 32 * 32 * 64)])
+@pytest.mark.parametrize("kind,mnk", [(0, 32 * 32 * 16), (1, 32 * 32 * 64), (2, 16 * 16 * 32)])
 def test_mfma_stream_runs_and_counts(gpu_lib, kind, mnk):
     print(f"[case] mfma stream kind {kind}", flush=True)
     n_cu = torch.cuda.get_device_properties(0).multi_processor_count
