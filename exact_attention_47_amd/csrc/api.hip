@@ -60,12 +60,13 @@ size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // Short key ranges run on the short-range kernel (three or four small
 // workgroups per CU hide one another's start-up and memory waits), long ones
-// on the main kernel. Crossovers measured on the sweeps: D = 64 up to 4096
-// keys (+33 % at 512, +2 % at 4096, -1 to -2.6 % at 8192 and 16384), causal
-// D = 64 up to 8192 (+4.8 % at 8192; at 16384 +1 % with 32 heads, -7 % with
-// 8), D = 128 causal up to 2048 (+14 % at 512, equal at 4096, -6 % at 8192),
-// D = 128 non-causal up to 1024 (+16 % at 512, -2 % at 2048). Requested
-// splits always go to the main kernel, whose key tile the split plan uses.
+// on the main kernel. Crossovers measured on the sweeps (short-range over
+// main kernel; run-to-run spread about 1.5 %): D = 64 up to 4096 keys (+17 %
+// at 1024, +4.5 % at 2048, -1.4 % at 4096), causal D = 64 up to 8192 (+9 % at
+// 2048, +14 % at 4096, +5.6 % at 8192, equal at 16384), D = 128 causal up to
+// 2048 (+20 % at 512, +2.6 % at 1024, +1.4 % at 2048, equal at 4096), D = 128
+// non-causal up to 1024 (+13 % at 512, +2.4 % at 1024). Requested splits
+// always go to the main kernel, whose key tile the split plan uses.
 bool use_short_kernel(int D, int causal, int S_k, int n_split) {
   if (n_split != 1) return false;
   if (D == 64) return S_k <= (causal ? 8192 : 4096);
@@ -75,7 +76,10 @@ bool use_short_kernel(int D, int causal, int S_k, int n_split) {
 
 // Causal D = 128 on the main kernel runs on the persistent grid: its snake
 // deal measured +0.8 to +2 % over the hardware-dealt grid from 4K to 16K
-// keys; D = 64 (-1 %) and non-causal work (+0.5 %) keep the plain grid.
+// keys on the 32x32x16 form of the kernel; on the 16x16x32 form the two
+// grids are within 0.7 % of each other there, and D = 64 and non-causal work
+// gain 0.1 to 1.4 % on the persistent grid (all within the run-to-run
+// spread), so the choice stands.
 bool use_persistent(int D, int causal, int n_split) { return causal && D == 128 && n_split == 1; }
 
 // Compute units of the current device, asked once per device.
