@@ -140,10 +140,10 @@ fwd_mfma_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
   // A persistent grid (PERSIST) runs this body once per work item it is
   // dealt; otherwise there is one workgroup per item and one pass.
   for (int it = 0;; it++) {
-  // (per item, the lane index passes through an empty asm statement so that
-  // no lane-dependent value is hoisted out of the item loop, where it would
-  // hold a register across every item)
-  int lane = tid & 63;
+  // (per item, the lane index is read afresh and passes through an empty asm
+  // statement, so that no lane-dependent value is hoisted out of the item
+  // loop, where it would hold a register across every item)
+  int lane = PERSIST ? (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)) : tid & 63;
   if (PERSIST) asm volatile("" : "+v"(lane));
   const int g = lane >> 4;         // 16-lane group: rows 4g..4g+3 of each 16 x 16 output block
   const int n = lane & 15;         // query column within a 16-query block
@@ -500,10 +500,16 @@ fwd_mfma_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
     if (grp == 0) barrier();
   }
 
-  // ---- epilogue: normalise, logsumexp, store
+  // ---- epilogue: normalise, logsumexp, store. The lane index passes
+  // through an empty asm statement here too: otherwise the compiler shares
+  // the row addresses of the Q loads with the O stores and keeps them live
+  // across the tile loop (8-10 registers, which spilled on some variants).
+  int lane_e = lane;
+  asm volatile("" : "+v"(lane_e));
+  const int n_e = lane_e & 15, g_e = lane_e >> 4;
 #pragma unroll
   for (int qb = 0; qb < 2; qb++) {
-    const int q = wr0 + qb * 16 + n;
+    const int q = wr0 + qb * 16 + n_e;
     const float lt = quad_sum(l[qb]);
     const bool has = m[qb] != kNegInf && lt > 0.0f;
     const float inv = has ? 1.0f / lt : 0.0f;
@@ -517,9 +523,9 @@ fwd_mfma_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
           v4t w;
 #pragma unroll
           for (int e = 0; e < 4; e++) w[e] = (T)(o[db][qb][e] * inv);
-          *(v4t*)(orow + db * 16 + 4 * g) = w;
+          *(v4t*)(orow + db * 16 + 4 * g_e) = w;
         }
-        if (g == 0) lseh[q] = lse;
+        if (g_e == 0) lseh[q] = lse;
       } else {
         const size_t prow = ((size_t)split * BH + bh) * S_q + q;
         float* orow = Opart + prow * D;
@@ -530,9 +536,9 @@ fwd_mfma_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
           w.y = o[db][qb][1] * inv;
           w.z = o[db][qb][2] * inv;
           w.w = o[db][qb][3] * inv;
-          *(float4*)(orow + db * 16 + 4 * g) = w;
+          *(float4*)(orow + db * 16 + 4 * g_e) = w;
         }
-        if (g == 0) Lpart[prow] = lse;
+        if (g_e == 0) Lpart[prow] = lse;
       }
     }
   }
