@@ -11,8 +11,9 @@
 //
 // Three launches of one kernel template share the forward kernel's operand
 // layout (a 32-row "outer" block per wave held in registers as the B operand,
-// 32-row "inner" tiles streamed through LDS, accumulators transposed so that
-// one lane owns one outer row):
+// 32-row "inner" tiles streamed through LDS, every product on the 16x16x32
+// MFMA with accumulators transposed so that lane (g, n) owns outer rows n and
+// 16 + n and holds inner rows 4g .. 4g+3 of each 16-row inner block):
 //
 //   mode dQ: outer = query rows, inner = keys:  S^T = K Q^T, dP^T = V dO^T,
 //            dQ^T += K^T dS^T
@@ -27,9 +28,10 @@
 // are deterministic (no atomics). At D = 64 both accumulators fit, and the
 // dKV mode needs seven products. The A operands of the accumulations (K^T,
 // Q^T, dO^T) are read from the staged tiles with ds_read_b64_tr_b16, choosing
-// for each k slot the inner row that the probability fragment holds there,
-// exactly as the forward pass reads V^T. Staged tiles use an XOR swizzle that
-// suits both read patterns (see bswz).
+// for each k slot the inner row that the probability fragment holds there
+// (a lane's four rows of inner block 0, then its four of block 1), exactly as
+// the forward pass reads V^T. Staged tiles use an XOR swizzle that suits both
+// read patterns (see bswz).
 //
 // A small first kernel (one row per D/8 lanes, float32 sum) writes -Dd and
 // -log2(e) LSE per query row, the forms the tiles consume: P = exp2(S c +
@@ -45,15 +47,15 @@ namespace {
 template <typename T> struct BMma;
 template <> struct BMma<__bf16> {
   typedef v8bf16 frag;
-  static __device__ __forceinline__ v16f mma(frag a, frag b, v16f c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  static __device__ __forceinline__ v4f mma(frag a, frag b, v4f c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
   }
   static __device__ __forceinline__ frag cvt(v8f x) { return __builtin_convertvector(x, v8bf16); }
 };
 template <> struct BMma<_Float16> {
   typedef v8f16 frag;
-  static __device__ __forceinline__ v16f mma(frag a, frag b, v16f c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  static __device__ __forceinline__ v4f mma(frag a, frag b, v4f c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
   }
   static __device__ __forceinline__ frag cvt(v8f x) { return __builtin_convertvector(x, v8f16); }
 };
@@ -66,8 +68,8 @@ struct BwdCfg {
   static constexpr int NT = NW * 64;
   static constexpr int BO = NW * 32;            // outer rows per workgroup
   static constexpr int BI = 32;                 // inner rows per tile
-  static constexpr int DS = D / 16;             // k-steps over D
-  static constexpr int DB = D / 32;             // 32-wide blocks of D
+  static constexpr int DS = D / 32;             // k-steps over D
+  static constexpr int DB = D / 16;             // 16-wide blocks of D
   static constexpr int RB = 2 * D;              // bytes per row
   static constexpr int TILE = BI * RB;
   static constexpr int STAGE = 2 * TILE + 512;  // X, Y, then 64 -log2(e) LSE and 64 -Dd values (inner = queries)
@@ -77,13 +79,14 @@ struct BwdCfg {
 };
 
 // Row-dependent 16-byte-chunk XOR swizzle of the staged tiles, which are read
-// both by rows (16 lanes: one chunk of 16 consecutive rows) and transposed
-// (32 lanes: four chunks of 4 consecutive rows). At D = 128 (16 chunks per
-// row) ((r & 3) << 2) | ((r >> 2) & 3) gives 16 consecutive rows 16 distinct
-// values and 4 aligned rows 4 distinct quarters, so both patterns touch
-// every bank once; D = 64 keeps the row-read swizzle of the forward pass.
+// both by rows (16 lanes per LDS cycle: one chunk of each of 16 consecutive
+// rows) and transposed (32 lanes: one 32-byte segment of each of 8
+// consecutive rows). At D = 128 (16 chunks per row) ((r & 7) << 1) | ((r >> 3)
+// & 1) gives 16 aligned rows 16 distinct chunks and 8 aligned rows 8 distinct
+// segments; at D = 64 odd rows start on bank 32, and the same is done with the
+// row bits above the lowest. Both patterns touch every bank once.
 template <int D> __device__ __forceinline__ int bswz(int r) {
-  return D == 64 ? (r >> 1) & 7 : ((r & 3) << 2) | ((r >> 2) & 3);
+  return D == 64 ? (((r >> 1) & 3) << 1) | ((r >> 3) & 1) : ((r & 7) << 1) | ((r >> 3) & 1);
 }
 
 template <typename T>
@@ -142,8 +145,8 @@ bwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int hh = lane >> 5;
-  const int nn = lane & 31;
+  const int g = lane >> 4;                      // 16-lane group: inner rows 4g..4g+3 of each 16-row block
+  const int n = lane & 15;                      // outer rows n and 16 + n of the wave
 
   int ot, bh;
   if (!CAUSAL) {
@@ -183,33 +186,37 @@ bwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict
   const float* nl2h = NL2 + (size_t)bh * S_q;   // -log2(e) LSE
   const float* nddh = NDd + (size_t)bh * S_q;   // -Dd
 
-  // outer rows as B operands: lane (h, n) holds row wr0+n, d = 16 ds + 8 h .. +7
-  frag of1[C::DS], of2[TWO ? C::DS : 1];
-  {
-    const int r = wr0 + nn;
+  // outer rows as B operands: lane (g, n) holds row wr0 + 16 ob + n, d = 32 ds + 8 g .. +7
+  frag of1[C::DS][2], of2[TWO ? C::DS : 1][2];
+#pragma unroll
+  for (int ob = 0; ob < 2; ob++) {
+    const int r = wr0 + 16 * ob + n;
 #pragma unroll
     for (int ds = 0; ds < C::DS; ds++) {
       if (r < S_o) {
-        of1[ds] = *(const frag*)(O1 + (size_t)r * D + ds * 16 + 8 * hh);
-        if constexpr (TWO) of2[ds] = *(const frag*)(O2 + (size_t)r * D + ds * 16 + 8 * hh);
+        of1[ds][ob] = *(const frag*)(O1 + (size_t)r * D + ds * 32 + 8 * g);
+        if constexpr (TWO) of2[ds][ob] = *(const frag*)(O2 + (size_t)r * D + ds * 32 + 8 * g);
       } else {
 #pragma unroll
         for (int e = 0; e < 8; e++) {
-          of1[ds][e] = (T)0.0f;
-          if constexpr (TWO) of2[ds][e] = (T)0.0f;
+          of1[ds][ob][e] = (T)0.0f;
+          if constexpr (TWO) of2[ds][ob][e] = (T)0.0f;
         }
       }
     }
   }
-  // per-lane scalars of the outer query row (mode dQ)
-  float nl2_o = 0.0f, ndd_o = 0.0f;
-  if (DQ && wr0 + nn < S_q) {
-    nl2_o = nl2h[wr0 + nn];
-    ndd_o = nddh[wr0 + nn];
-  }
-  v16f dd_init;
+  // per-lane scalars of the outer query rows (mode dQ)
+  float nl2_o[2] = {0.0f, 0.0f}, ndd_o[2] = {0.0f, 0.0f};
+  if (DQ) {
 #pragma unroll
-  for (int e = 0; e < 16; e++) dd_init[e] = ndd_o;
+    for (int ob = 0; ob < 2; ob++) {
+      const int r = wr0 + 16 * ob + n;
+      if (r < S_q) {
+        nl2_o[ob] = nl2h[r];
+        ndd_o[ob] = nddh[r];
+      }
+    }
+  }
 
   // stage t: X rows 32t.., Y rows 32t.. (buffer loads; rows past the end read 0)
   const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc((void*)Xg, (short)0, S_i * C::RB, 0x00020000);
@@ -243,36 +250,36 @@ bwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict
     }
   };
 
-  // LDS read offsets: row reads (A of the two products) and transposed reads
-  // (A of the accumulation)
-  constexpr int NKR = C::DS < 8 ? C::DS : 8;
-  const int xk = bswz<D>(nn);
-  int k_rd[NKR];
+  // LDS read offsets (the swizzle depends on the low four row bits only, so
+  // the offsets of inner block 1 are those of block 0 plus 16 rows).
+  // Row reads (A of the two products): inner row n, chunk 4 ds + g.
+  int k_rd[C::DS];
 #pragma unroll
-  for (int ds = 0; ds < NKR; ds++) k_rd[ds] = nn * C::RB + (((2 * ds + hh) ^ xk) * 16);
-  const int g = lane >> 4, jj = lane & 15;
-  const int vrow = 4 * hh + (jj >> 2);          // inner row = vrow + 16 ks + 8 part
-  const int x0 = bswz<D>(vrow), x1 = bswz<D>(vrow + 8);
-  int tr_lo[C::DB], tr_hi[C::DB];
+  for (int ds = 0; ds < C::DS; ds++) k_rd[ds] = n * C::RB + (((4 * ds + g) ^ bswz<D>(n)) * 16);
+  // Transposed reads (A of the accumulations): lane n of group g addresses
+  // inner row 4g + n/4 (and 16 rows further), columns 16 db + 4 (n % 4) .. +3.
+  const int vrow = 4 * g + (n >> 2);
+  int tr_rd[C::DB];
 #pragma unroll
-  for (int db = 0; db < C::DB; db++) {
-    const int chunk = 4 * db + 2 * (g & 1) + ((jj & 3) >> 1);
-    tr_lo[db] = vrow * C::RB + ((chunk ^ x0) * 16) + 8 * (jj & 1);
-    tr_hi[db] = (vrow + 8) * C::RB + ((chunk ^ x1) * 16) + 8 * (jj & 1);
-  }
+  for (int db = 0; db < C::DB; db++)
+    tr_rd[db] = vrow * C::RB + (((2 * db + ((n & 3) >> 1)) ^ bswz<D>(vrow)) * 16) + 8 * (n & 1);
 
-  v16f acc[C::DB];
+  v4f acc[C::DB][2];
 #pragma unroll
   for (int db = 0; db < C::DB; db++)
 #pragma unroll
-    for (int e = 0; e < 16; e++) acc[db][e] = 0.0f;
+    for (int ob = 0; ob < 2; ob++)
+#pragma unroll
+      for (int e = 0; e < 4; e++) acc[db][ob][e] = 0.0f;
   // second accumulator (mode kDKV: dV^T next to dK^T)
   constexpr int DB2 = MODE == kDKV ? C::DB : 1;
-  v16f acc2[DB2];
+  v4f acc2[DB2][2];
 #pragma unroll
   for (int db = 0; db < DB2; db++)
 #pragma unroll
-    for (int e = 0; e < 16; e++) acc2[db][e] = 0.0f;
+    for (int ob = 0; ob < 2; ob++)
+#pragma unroll
+      for (int e = 0; e < 4; e++) acc2[db][ob][e] = 0.0f;
 
   auto barrier = [] {
     asm volatile("" ::: "memory");
@@ -282,115 +289,129 @@ bwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict
     asm volatile("" ::: "memory");
   };
 
+  // acc^T[d x outer] += Z^T[d x inner] F[inner x outer] for one staged tile Z
+  auto accumulate = [&](v4f (*dst)[2], const char* zs, const frag* f) {
+#pragma unroll
+    for (int db = 0; db < C::DB; db++) {
+      v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(zs + tr_rd[db]));
+      v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(zs + tr_rd[db] + 16 * C::RB));
+      const frag a = __builtin_bit_cast(frag, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      dst[db][0] = M::mma(a, f[0], dst[db][0]);
+      dst[db][1] = M::mma(a, f[1], dst[db][1]);
+    }
+  };
+
   auto step = [&](int t, const char* st) {
     const char* xs = st;
     const char* ys = st + C::TILE;
-    // C[inner 32 x outer 32] = X_tile O1^T (lane (h, n): outer row n, inner rows 8i + 4h + j)
-    v16f s;
+    // C[inner 32 x outer 32] = X_tile O1^T: block (ib, ob) of lane (g, n) holds
+    // inner rows 16 ib + 4g + i of outer row 16 ob + n
+    v4f s[2][2];
 #pragma unroll
-    for (int e = 0; e < 16; e++) s[e] = 0.0f;
+    for (int ds = 0; ds < C::DS; ds++)
 #pragma unroll
-    for (int ds = 0; ds < C::DS; ds++) {
-      const frag a = *(const frag*)(xs + k_rd[ds % NKR] + (ds / NKR) * 256);
-      s = M::mma(a, of1[ds], s);
-    }
-    v16f dp = {};
+      for (int ib = 0; ib < 2; ib++) {
+        const frag a = *(const frag*)(xs + k_rd[ds] + ib * 16 * C::RB);
+        if (ds == 0) {
+          const v4f zero = {};
+          s[ib][0] = M::mma(a, of1[ds][0], zero);
+          s[ib][1] = M::mma(a, of1[ds][1], zero);
+        } else {
+          s[ib][0] = M::mma(a, of1[ds][0], s[ib][0]);
+          s[ib][1] = M::mma(a, of1[ds][1], s[ib][1]);
+        }
+      }
+    v4f dp[2][2] = {};
     if constexpr (TWO) {
-      if constexpr (DQ) {
-        // every element of a lane belongs to its outer (query) row: the
-        // product starts from a register block that holds that row's -Dd
-        dp = dd_init;
-      } else {
-        // dP - Dd in one product: the accumulator starts at the staged -Dd of
-        // the inner (query) row that each element belongs to
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-          const float4 d4 = *(const float4*)(st + 2 * C::TILE + 256 + (8 * i + 4 * hh) * 4);
-          dp[4 * i + 0] = d4.x; dp[4 * i + 1] = d4.y; dp[4 * i + 2] = d4.z; dp[4 * i + 3] = d4.w;
+      for (int ib = 0; ib < 2; ib++) {
+        if constexpr (DQ) {
+          // every element of a block belongs to its outer (query) row: the
+          // product starts from that row's -Dd
+#pragma unroll
+          for (int ob = 0; ob < 2; ob++)
+#pragma unroll
+            for (int e = 0; e < 4; e++) dp[ib][ob][e] = ndd_o[ob];
+        } else {
+          // dP - Dd in one product: the accumulator starts at the staged -Dd
+          // of the inner (query) row that each element belongs to
+          const float4 d4 = *(const float4*)(st + 2 * C::TILE + 256 + (16 * ib + 4 * g) * 4);
+#pragma unroll
+          for (int ob = 0; ob < 2; ob++) {
+            dp[ib][ob][0] = d4.x; dp[ib][ob][1] = d4.y; dp[ib][ob][2] = d4.z; dp[ib][ob][3] = d4.w;
+          }
         }
       }
 #pragma unroll
-      for (int ds = 0; ds < C::DS; ds++) {
-        const frag a = *(const frag*)(ys + k_rd[ds % NKR] + (ds / NKR) * 256);
-        dp = M::mma(a, of2[ds], dp);
-      }
+      for (int ds = 0; ds < C::DS; ds++)
+#pragma unroll
+        for (int ib = 0; ib < 2; ib++) {
+          const frag a = *(const frag*)(ys + k_rd[ds] + ib * 16 * C::RB);
+          dp[ib][0] = M::mma(a, of2[ds][0], dp[ib][0]);
+          dp[ib][1] = M::mma(a, of2[ds][1], dp[ib][1]);
+        }
     }
     // probabilities (and dS), masked where the key is outside the range or
     // after the causal limit. The mask is evaluated only on tiles that hold
     // such a pair for this wave's 32 outer rows (range tails, the causal
     // diagonal); elsewhere every pair is allowed.
-    const int orow = wr0 + nn;
     const int t0 = t * C::BI;
     const bool full = DQ ? (wr0 + 32 <= S_q && t0 + C::BI <= S_k && (!CAUSAL || t0 + C::BI - 1 <= wr0 + diag))
                          : (t0 + C::BI <= S_q && wr0 + 32 <= S_k && (!CAUSAL || wr0 + 31 <= t0 + diag));
-    float gv[16], gp[16];
+    float gv[2][2][4], gp[2][2][4];
     auto probs = [&](auto masked) {
       constexpr bool MASKED = decltype(masked)::value;
 #pragma unroll
-      for (int i = 0; i < 4; i++) {
-        float l4[4];
-        const int ir0 = t0 + 8 * i + 4 * hh;          // inner rows ir0 .. ir0+3
+      for (int ib = 0; ib < 2; ib++) {
+        const int ir0 = t0 + 16 * ib + 4 * g;          // inner rows ir0 .. ir0+3
+        float l4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
         if (!DQ) {
-          const float4 lv = *(const float4*)(st + 2 * C::TILE + (8 * i + 4 * hh) * 4);
+          const float4 lv = *(const float4*)(st + 2 * C::TILE + (16 * ib + 4 * g) * 4);
           l4[0] = lv.x; l4[1] = lv.y; l4[2] = lv.z; l4[3] = lv.w;
         }
 #pragma unroll
-        for (int j = 0; j < 4; j++) {
-          const int e = 4 * i + j;
-          const int ir = ir0 + j;
-          const int query = DQ ? orow : ir;
-          const int key = DQ ? ir : orow;
-          const bool ok = !MASKED || (query < S_q && key < S_k && (!CAUSAL || key <= query + diag));
-          const float nl2 = DQ ? nl2_o : l4[j];
-          const float p = ok ? fast_exp2(__builtin_fmaf(s[e], c, nl2)) : 0.0f;
-          if (MODE == kDV) gv[e] = p;
-          else gv[e] = p * dp[e];                    // dp already holds dP - Dd
-          if (MODE == kDKV) gp[e] = p;
+        for (int ob = 0; ob < 2; ob++) {
+          const int orow = wr0 + 16 * ob + n;
+#pragma unroll
+          for (int i = 0; i < 4; i++) {
+            const int ir = ir0 + i;
+            const int query = DQ ? orow : ir;
+            const int key = DQ ? ir : orow;
+            const bool ok = !MASKED || (query < S_q && key < S_k && (!CAUSAL || key <= query + diag));
+            const float nl2 = DQ ? nl2_o[ob] : l4[i];
+            const float p = ok ? fast_exp2(__builtin_fmaf(s[ib][ob][i], c, nl2)) : 0.0f;
+            if (MODE == kDV) gv[ib][ob][i] = p;
+            else gv[ib][ob][i] = p * dp[ib][ob][i];     // dp already holds dP - Dd
+            if (MODE == kDKV) gp[ib][ob][i] = p;
+          }
         }
       }
     };
     if (full) probs(BIC<false>());
     else probs(BIC<true>());
+    // B operand of the accumulation, k order: the lane's four rows of inner
+    // block 0, then its four of block 1
     frag gf[2];
 #pragma unroll
-    for (int ks = 0; ks < 2; ks++) {
+    for (int ob = 0; ob < 2; ob++) {
       v8f w;
 #pragma unroll
-      for (int e = 0; e < 8; e++) w[e] = gv[8 * ks + e];
-      gf[ks] = M::cvt(w);
+      for (int e = 0; e < 8; e++) w[e] = gv[e >> 2][ob][e & 3];
+      gf[ob] = M::cvt(w);
     }
-    // acc^T[d x outer] += Z^T[d x inner] G[inner x outer], Z = X (dQ, dK) or Y (dV)
-    const char* zs = MODE == kDV ? ys : xs;
-#pragma unroll
-    for (int ks = 0; ks < 2; ks++)
-#pragma unroll
-      for (int db = 0; db < C::DB; db++) {
-        const char* za = zs + 16 * ks * C::RB;
-        v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(za + tr_lo[db]));
-        v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(za + tr_hi[db]));
-        const frag a = __builtin_bit_cast(frag, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        acc[db] = M::mma(a, gf[ks], acc[db]);
-      }
+    // acc^T += Z^T G, Z = X (dQ, dK) or Y (dV)
+    accumulate(acc, MODE == kDV ? ys : xs, gf);
     if constexpr (MODE == kDKV) {
       // dV^T[d x outer] += dO^T[d x inner] P[inner x outer], from the same stage
       frag pf2[2];
 #pragma unroll
-      for (int ks = 0; ks < 2; ks++) {
+      for (int ob = 0; ob < 2; ob++) {
         v8f w;
 #pragma unroll
-        for (int e = 0; e < 8; e++) w[e] = gp[8 * ks + e];
-        pf2[ks] = M::cvt(w);
+        for (int e = 0; e < 8; e++) w[e] = gp[e >> 2][ob][e & 3];
+        pf2[ob] = M::cvt(w);
       }
-#pragma unroll
-      for (int ks = 0; ks < 2; ks++)
-#pragma unroll
-        for (int db = 0; db < C::DB; db++) {
-          const char* za = ys + 16 * ks * C::RB;
-          v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(za + tr_lo[db]));
-          v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(za + tr_hi[db]));
-          const frag a = __builtin_bit_cast(frag, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-          acc2[db] = M::mma(a, pf2[ks], acc2[db]);
-        }
+      accumulate(acc2, ys, pf2);
     }
   };
 
@@ -419,33 +440,31 @@ bwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict
     }
   }
 
-  // store the gradient rows of this wave: lane (h, n) holds row wr0+n,
-  // columns 32 db + 8 i + 4 h + j
-  const int r = wr0 + nn;
-  if (r < S_o) {
-    T* grow = Gout + (size_t)bh * S_o * D + (size_t)r * D;
+  // store the gradient rows of this wave: lane (g, n) holds rows wr0 + 16 ob
+  // + n, columns 16 db + 4g .. +3
 #pragma unroll
-    for (int db = 0; db < C::DB; db++)
+  for (int ob = 0; ob < 2; ob++) {
+    const int r = wr0 + 16 * ob + n;
+    if (r < S_o) {
+      typedef T v4t __attribute__((ext_vector_type(4)));
+      T* grow = Gout + (size_t)bh * S_o * D + (size_t)r * D;
 #pragma unroll
-      for (int i = 0; i < 4; i++) {
-        typedef T v4t __attribute__((ext_vector_type(4)));
+      for (int db = 0; db < C::DB; db++) {
         v4t w;
 #pragma unroll
-        for (int j = 0; j < 4; j++) w[j] = (T)(acc[db][4 * i + j] * gscale);
-        *(v4t*)(grow + db * 32 + 8 * i + 4 * hh) = w;
+        for (int e = 0; e < 4; e++) w[e] = (T)(acc[db][ob][e] * gscale);
+        *(v4t*)(grow + db * 16 + 4 * g) = w;
       }
-    if constexpr (MODE == kDKV) {
-      T* grow2 = Gout2 + (size_t)bh * S_o * D + (size_t)r * D;
+      if constexpr (MODE == kDKV) {
+        T* grow2 = Gout2 + (size_t)bh * S_o * D + (size_t)r * D;
 #pragma unroll
-      for (int db = 0; db < DB2; db++)
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-          typedef T v4t __attribute__((ext_vector_type(4)));
+        for (int db = 0; db < DB2; db++) {
           v4t w;
 #pragma unroll
-          for (int j = 0; j < 4; j++) w[j] = (T)acc2[db][4 * i + j];
-          *(v4t*)(grow2 + db * 32 + 8 * i + 4 * hh) = w;
+          for (int e = 0; e < 4; e++) w[e] = (T)acc2[db][ob][e];
+          *(v4t*)(grow2 + db * 16 + 4 * g) = w;
         }
+      }
     }
   }
 }
