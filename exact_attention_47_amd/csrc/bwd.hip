@@ -9,24 +9,23 @@
 //   dV = P^T dO,  dP = dO V^T,  dS = P * (dP - Dd),  Dd_i = sum_d dO_id O_id,
 //   dQ = scale dS K,  dK = scale dS^T Q.
 //
-// Three launches of one kernel template share the forward kernel's operand
-// layout (a 32-row "outer" block per wave held in registers as the B operand,
-// 32-row "inner" tiles streamed through LDS, every product on the 16x16x32
-// MFMA with accumulators transposed so that lane (g, n) owns outer rows n and
-// 16 + n and holds inner rows 4g .. 4g+3 of each 16-row inner block):
+// Two launches of one kernel template share the forward kernel's operand
+// layout (a 32-row "outer" block per wave held as the B operand, 32-row
+// "inner" tiles streamed through LDS, every product on the 16x16x32 MFMA with
+// accumulators transposed so that lane (g, n) owns outer rows n and 16 + n
+// and holds inner rows 4g .. 4g+3 of each 16-row inner block):
 //
-//   mode dQ: outer = query rows, inner = keys:  S^T = K Q^T, dP^T = V dO^T,
-//            dQ^T += K^T dS^T
-//   mode dK: outer = keys, inner = query rows:  S = Q K^T,  dP = dO V^T,
-//            dK^T += Q^T dS
-//   mode dV: outer = keys, inner = query rows:  S = Q K^T,  dV^T += dO^T P
-//   mode dKV (D = 64): the dK and dV modes in one pass, S and P computed once
+//   mode dQ:  outer = query rows, inner = keys:  S^T = K Q^T, dP^T = V dO^T,
+//             dQ^T += K^T dS^T
+//   mode dKV: outer = keys, inner = query rows:  S = Q K^T,  dP = dO V^T,
+//             dK^T += Q^T dS,  dV^T += dO^T P
 //
-// Splitting dK and dV recomputes S once more (eight products per tile pair
-// instead of five) but keeps each wave under the 256 registers that two waves
-// per SIMD allow, and every gradient is a plain sum in a fixed order: results
-// are deterministic (no atomics). At D = 64 both accumulators fit, and the
-// dKV mode needs seven products. The A operands of the accumulations (K^T,
+// dQ and dKV each compute S and P (seven products per tile pair instead of
+// five), and every gradient is a plain sum in a fixed order: results are
+// deterministic (no atomics). At D = 128 the dKV mode's two accumulators and
+// the outer K rows fill the 256 registers of two waves per SIMD, so its outer
+// V rows (the B operand of dP) are read from LDS. The A operands of the
+// accumulations (K^T,
 // Q^T, dO^T) are read from the staged tiles with ds_read_b64_tr_b16, choosing
 // for each k slot the inner row that the probability fragment holds there
 // (a lane's four rows of inner block 0, then its four of block 1), exactly as
@@ -35,8 +34,8 @@
 //
 // A small first kernel (one row per D/8 lanes, float32 sum) writes -Dd and
 // -log2(e) LSE per query row, the forms the tiles consume: P = exp2(S c +
-// (-log2(e) LSE)) is one multiply-add and an exp2, and dK's dP product starts
-// its accumulator at -Dd, so that dS = P * dP is one multiply.
+// (-log2(e) LSE)) is one multiply-add and an exp2, and dKV's dP product
+// starts its accumulator at -Dd, so that dS = P * dP is one multiply.
 #include "common.h"
 #include "kernels.h"
 
@@ -60,7 +59,7 @@ template <> struct BMma<_Float16> {
   static __device__ __forceinline__ frag cvt(v8f x) { return __builtin_convertvector(x, v8f16); }
 };
 
-constexpr int kDQ = 0, kDK = 1, kDV = 2, kDKV = 3;   // kDKV: dK and dV in one pass
+constexpr int kDQ = 0, kDKV = 1;   // dQ; dK and dV in one pass
 
 template <int D>
 struct BwdCfg {
@@ -131,7 +130,7 @@ template <bool B> struct BIC { static constexpr bool value = B; };
 
 template <typename T, int D, int MODE, bool CAUSAL>
 __global__ void __launch_bounds__(256)
-__attribute__((amdgpu_waves_per_eu(MODE == 2 ? 3 : 2, MODE == 2 ? 3 : 2)))
+__attribute__((amdgpu_waves_per_eu(2, 2)))
 bwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
            const T* __restrict__ dO, const float* __restrict__ NL2, const float* __restrict__ NDd,
            T* __restrict__ Gout, T* __restrict__ Gout2, int BH, int S_q, int S_k, int n_ot, float c,
@@ -141,9 +140,13 @@ bwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict
   using M = BMma<T>;
   typedef typename M::frag frag;
   constexpr bool DQ = MODE == kDQ;
-  constexpr bool TWO = MODE != kDV;             // second product dP needed
+  // dKV at D = 128: the outer V rows (B operand of dP) are read from LDS
+  // instead of registers, which keeps both accumulators within the 256
+  // registers of two waves per SIMD
+  constexpr bool OF2_LDS = !DQ && D == 128;
   __shared__ __attribute__((aligned(1024))) char st0[C::STAGE];
   __shared__ __attribute__((aligned(1024))) char st1[C::STAGE];
+  __shared__ __attribute__((aligned(1024))) char ovs[OF2_LDS ? C::BO * C::RB : 16];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -190,7 +193,8 @@ bwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict
   const float* nddh = NDd + (size_t)bh * S_q;   // -Dd
 
   // outer rows as B operands: lane (g, n) holds row wr0 + 16 ob + n, d = 32 ds + 8 g .. +7
-  frag of1[C::DS][2], of2[TWO ? C::DS : 1][2];
+  constexpr bool OF2_REG = !OF2_LDS;
+  frag of1[C::DS][2], of2[OF2_REG ? C::DS : 1][2];
 #pragma unroll
   for (int ob = 0; ob < 2; ob++) {
     const int r = wr0 + 16 * ob + n;
@@ -198,15 +202,30 @@ bwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict
     for (int ds = 0; ds < C::DS; ds++) {
       if (r < S_o) {
         of1[ds][ob] = *(const frag*)(O1 + (size_t)r * D + ds * 32 + 8 * g);
-        if constexpr (TWO) of2[ds][ob] = *(const frag*)(O2 + (size_t)r * D + ds * 32 + 8 * g);
+        if constexpr (OF2_REG) of2[ds][ob] = *(const frag*)(O2 + (size_t)r * D + ds * 32 + 8 * g);
       } else {
 #pragma unroll
         for (int e = 0; e < 8; e++) {
           of1[ds][ob][e] = (T)0.0f;
-          if constexpr (TWO) of2[ds][ob][e] = (T)0.0f;
+          if constexpr (OF2_REG) of2[ds][ob][e] = (T)0.0f;
         }
       }
     }
+  }
+  // OF2_LDS: each wave writes its 32 outer V rows to its 32-row slice of ovs
+  // (rows past S_o as zeros), with the staged tiles' swizzle, and reads them
+  // back with the row-read offsets below
+  if constexpr (OF2_LDS) {
+    char* ow = ovs + wave * 32 * C::RB;
+#pragma unroll
+    for (int i = 0; i < 32 * C::RB / (64 * 16); i++) {
+      const int cidx = i * 64 + lane;               // 16-byte chunk of the wave's slice
+      const int row = cidx / (C::RB / 16), u = cidx % (C::RB / 16);
+      uint4 val = make_uint4(0u, 0u, 0u, 0u);
+      if (wr0 + row < S_o) val = *(const uint4*)(O2 + (size_t)(wr0 + row) * D + u * 8);
+      *(uint4*)(ow + row * C::RB + ((u ^ bswz<D>(row)) * 16)) = val;
+    }
+    __syncthreads();
   }
   // per-lane scalars of the outer query rows (mode dQ)
   float nl2_o[2] = {0.0f, 0.0f}, ndd_o[2] = {0.0f, 0.0f};
@@ -238,8 +257,7 @@ bwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict
       char* dd = base + 2 * C::TILE + 256;
       const int off = (t * C::BI + lane) * 4;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(lrs, (__attribute__((address_space(3))) void*)ld, 4, off, 0, 0, 0);
-      if (MODE == kDK || MODE == kDKV)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(drs, (__attribute__((address_space(3))) void*)dd, 4, off, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(drs, (__attribute__((address_space(3))) void*)dd, 4, off, 0, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < C::NI; i++) {
@@ -274,8 +292,8 @@ bwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict
     for (int ob = 0; ob < 2; ob++)
 #pragma unroll
       for (int e = 0; e < 4; e++) acc[db][ob][e] = 0.0f;
-  // second accumulator (mode kDKV: dV^T next to dK^T)
-  constexpr int DB2 = MODE == kDKV ? C::DB : 1;
+  // second accumulator (mode dKV: dV^T next to dK^T)
+  constexpr int DB2 = DQ ? 1 : C::DB;
   v4f acc2[DB2][2];
 #pragma unroll
   for (int db = 0; db < DB2; db++)
@@ -324,35 +342,43 @@ bwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict
           s[ib][1] = M::mma(a, of1[ds][1], s[ib][1]);
         }
       }
-    v4f dp[2][2] = {};
-    if constexpr (TWO) {
+    v4f dp[2][2];
 #pragma unroll
-      for (int ib = 0; ib < 2; ib++) {
-        if constexpr (DQ) {
-          // every element of a block belongs to its outer (query) row: the
-          // product starts from that row's -Dd
+    for (int ib = 0; ib < 2; ib++) {
+      if constexpr (DQ) {
+        // every element of a block belongs to its outer (query) row: the
+        // product starts from that row's -Dd
 #pragma unroll
-          for (int ob = 0; ob < 2; ob++)
+        for (int ob = 0; ob < 2; ob++)
 #pragma unroll
-            for (int e = 0; e < 4; e++) dp[ib][ob][e] = ndd_o[ob];
-        } else {
-          // dP - Dd in one product: the accumulator starts at the staged -Dd
-          // of the inner (query) row that each element belongs to
-          const float4 d4 = *(const float4*)(st + 2 * C::TILE + 256 + (16 * ib + 4 * g) * 4);
+          for (int e = 0; e < 4; e++) dp[ib][ob][e] = ndd_o[ob];
+      } else {
+        // dP - Dd in one product: the accumulator starts at the staged -Dd
+        // of the inner (query) row that each element belongs to
+        const float4 d4 = *(const float4*)(st + 2 * C::TILE + 256 + (16 * ib + 4 * g) * 4);
 #pragma unroll
-          for (int ob = 0; ob < 2; ob++) {
-            dp[ib][ob][0] = d4.x; dp[ib][ob][1] = d4.y; dp[ib][ob][2] = d4.z; dp[ib][ob][3] = d4.w;
-          }
+        for (int ob = 0; ob < 2; ob++) {
+          dp[ib][ob][0] = d4.x; dp[ib][ob][1] = d4.y; dp[ib][ob][2] = d4.z; dp[ib][ob][3] = d4.w;
         }
       }
+    }
 #pragma unroll
-      for (int ds = 0; ds < C::DS; ds++)
+    for (int ds = 0; ds < C::DS; ds++) {
+      frag b0, b1;
+      if constexpr (OF2_LDS) {
+        const char* ow = ovs + wave * 32 * C::RB;
+        b0 = *(const frag*)(ow + k_rd[ds]);
+        b1 = *(const frag*)(ow + k_rd[ds] + 16 * C::RB);
+      } else {
+        b0 = of2[ds][0];
+        b1 = of2[ds][1];
+      }
 #pragma unroll
-        for (int ib = 0; ib < 2; ib++) {
-          const frag a = *(const frag*)(ys + k_rd[ds] + ib * 16 * C::RB);
-          dp[ib][0] = M::mma(a, of2[ds][0], dp[ib][0]);
-          dp[ib][1] = M::mma(a, of2[ds][1], dp[ib][1]);
-        }
+      for (int ib = 0; ib < 2; ib++) {
+        const frag a = *(const frag*)(ys + k_rd[ds] + ib * 16 * C::RB);
+        dp[ib][0] = M::mma(a, b0, dp[ib][0]);
+        dp[ib][1] = M::mma(a, b1, dp[ib][1]);
+      }
     }
     // probabilities (and dS), masked where the key is outside the range or
     // after the causal limit. The mask is evaluated only on tiles that hold
@@ -383,9 +409,8 @@ bwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict
             const bool ok = !MASKED || (query < S_q && key < S_k && (!CAUSAL || key <= query + diag));
             const float nl2 = DQ ? nl2_o[ob] : l4[i];
             const float p = ok ? fast_exp2(__builtin_fmaf(s[ib][ob][i], c, nl2)) : 0.0f;
-            if (MODE == kDV) gv[ib][ob][i] = p;
-            else gv[ib][ob][i] = p * dp[ib][ob][i];     // dp already holds dP - Dd
-            if (MODE == kDKV) gp[ib][ob][i] = p;
+            gv[ib][ob][i] = p * dp[ib][ob][i];          // dp already holds dP - Dd
+            if (!DQ) gp[ib][ob][i] = p;
           }
         }
       }
@@ -402,9 +427,9 @@ bwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict
       for (int e = 0; e < 8; e++) w[e] = gv[e >> 2][ob][e & 3];
       gf[ob] = M::cvt(w);
     }
-    // acc^T += Z^T G, Z = X (dQ, dK) or Y (dV)
-    accumulate(acc, MODE == kDV ? ys : xs, gf);
-    if constexpr (MODE == kDKV) {
+    // acc^T += X^T dS (dQ^T += K^T dS^T, dK^T += Q^T dS)
+    accumulate(acc, xs, gf);
+    if constexpr (!DQ) {
       // dV^T[d x outer] += dO^T[d x inner] P[inner x outer], from the same stage
       frag pf2[2];
 #pragma unroll
@@ -458,7 +483,7 @@ bwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict
         for (int e = 0; e < 4; e++) w[e] = (T)(acc[db][ob][e] * gscale);
         *(v4t*)(grow + db * 16 + 4 * g) = w;
       }
-      if constexpr (MODE == kDKV) {
+      if constexpr (!DQ) {
         T* grow2 = Gout2 + (size_t)bh * S_o * D + (size_t)r * D;
 #pragma unroll
         for (int db = 0; db < DB2; db++) {
@@ -478,9 +503,9 @@ hipError_t launch_mode(const BwdArgs& a, hipStream_t st) {
   const int S_o = MODE == kDQ ? a.S_q : a.S_k;
   const int n_ot = (S_o + C::BO - 1) / C::BO;
   const dim3 grid((unsigned)(a.B * a.H * n_ot));
-  T* out = (T*)(MODE == kDQ ? a.dq : MODE == kDV ? a.dv : a.dk);
+  T* out = (T*)(MODE == kDQ ? a.dq : a.dk);
   T* out2 = (T*)(MODE == kDKV ? a.dv : nullptr);
-  const float gscale = MODE == kDV ? 1.0f : a.scale;
+  const float gscale = a.scale;
   if (a.causal)
     hipLaunchKernelGGL((bwd_kernel<T, D, MODE, true>), grid, dim3(C::NT), 0, st, (const T*)a.q, (const T*)a.k,
                        (const T*)a.v, (const T*)a.dout, a.nl2, a.dd, out, out2, a.B * a.H, a.S_q, a.S_k, n_ot,
@@ -503,16 +528,10 @@ hipError_t launch_d(const BwdArgs& a, hipStream_t st) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if ((e = launch_mode<T, D, kDQ>(a, st)) != hipSuccess) return e;
-  // D = 64: dK and dV in one pass (S and P computed once for both; 180
-  // VGPRs, +18 % on the whole backward at 4K). At D = 128 the second
-  // accumulator does not fit the 256 registers of two waves per SIMD (the
-  // fused pass spilled and ran 9-11 % slower), so dK and dV run separately.
-  if constexpr (D == 64) {
-    return launch_mode<T, D, kDKV>(a, st);
-  } else {
-    if ((e = launch_mode<T, D, kDK>(a, st)) != hipSuccess) return e;
-    return launch_mode<T, D, kDV>(a, st);
-  }
+  // dK and dV in one pass: S and P computed once for both (measured against
+  // separate dK and dV passes: +18 % on the whole backward at D = 64 4K,
+  // +11 to +13 % at D = 128 4K-16K, with the outer V rows in LDS there)
+  return launch_mode<T, D, kDKV>(a, st);
 }
 
 template <typename T>
