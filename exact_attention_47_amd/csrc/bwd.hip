@@ -469,10 +469,15 @@ bwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict
   }
 
   // store the gradient rows of this wave: lane (g, n) holds rows wr0 + 16 ob
-  // + n, columns 16 db + 4g .. +3
+  // + n, columns 16 db + 4g .. +3. The lane index passes through an empty asm
+  // statement, so that the compiler does not keep the outer rows' addresses
+  // live across the tile loop for these stores.
+  int lane_e = lane;
+  asm volatile("" : "+v"(lane_e));
+  const int n_e = lane_e & 15, g_e = lane_e >> 4;
 #pragma unroll
   for (int ob = 0; ob < 2; ob++) {
-    const int r = wr0 + 16 * ob + n;
+    const int r = wr0 + 16 * ob + n_e;
     if (r < S_o) {
       typedef T v4t __attribute__((ext_vector_type(4)));
       T* grow = Gout + (size_t)bh * S_o * D + (size_t)r * D;
@@ -481,7 +486,7 @@ bwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict
         v4t w;
 #pragma unroll
         for (int e = 0; e < 4; e++) w[e] = (T)(acc[db][ob][e] * gscale);
-        *(v4t*)(grow + db * 16 + 4 * g) = w;
+        *(v4t*)(grow + db * 16 + 4 * g_e) = w;
       }
       if constexpr (!DQ) {
         T* grow2 = Gout2 + (size_t)bh * S_o * D + (size_t)r * D;
@@ -490,7 +495,7 @@ bwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict
           v4t w;
 #pragma unroll
           for (int e = 0; e < 4; e++) w[e] = (T)acc2[db][ob][e];
-          *(v4t*)(grow2 + db * 16 + 4 * g) = w;
+          *(v4t*)(grow2 + db * 16 + 4 * g_e) = w;
         }
       }
     }
