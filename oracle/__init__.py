@@ -43,5 +43,5 @@ from .fp8 import (  # noqa: F401
     dequantize_blocks,
 )
 from .fp8_pipeline import (  # noqa: F401
-    fp8_attention_sim, fp8_attention_rows, p_rounding_bound, round_p, rmse, P_EXP_RANGE)
+    fp8_attention_sim, fp8_attention_rows, p_rounding_bound, p_rounding_lse_bound, round_p, rmse, P_EXP_RANGE)
 from .rope import rope_angles, rotary, rotary_f32, rope_hadamard_quantize  # noqa: F401

@@ -21,15 +21,19 @@ Attention is then the float64 definition on the dequantized values.
 
 The pages do not say how the probabilities enter the FP8 P V product. Reading:
 each p (relative to its row's maximum) is multiplied by 2^k, rounded to E4M3
-and divided by 2^k again, while the row sum l is taken from the unrounded p
-(``round_p``). The factor keeps small p out of the E4M3 subnormals. A kernel
+and divided by 2^k again (``round_p``), and the row sum l is the sum of those
+rounded values, so that O is the average of the V rows under the weights the
+product actually uses and the LSE is the log of their sum. The factor keeps
+small p out of the E4M3 subnormals. A kernel
 that forms p against a running reference which trails the row's final maximum
 by up to tau (log2) and scales by 2^k0 uses, relative to the final maximum,
 factors between 2^k0 and 2^(k0 + tau); the FP8 kernel of this repository has
 k0 = 7 and tau = 1.75. The simulation takes one factor 2^k for the whole row
 against the row's final maximum (no tiling); evaluated at k = 7 and k = 8.75
-it brackets that kernel's rounding. ``p_rounding_bound`` gives the largest
-error the rounding of P can cause in each output element for any k >= 7.
+it brackets that kernel's rounding. ``p_rounding_bound`` and
+``p_rounding_lse_bound`` give the largest error the rounding of P can cause in
+each output element and in each row's LSE for any k >= 7, whatever factor each
+p was rounded with.
 
 Parity unpinned: the absolute error values of this simulation are not printed
 by the pages; only the ratio between the two schemes is (2.6x), and that ratio
@@ -66,29 +70,56 @@ def round_p(p, p_exp: float = P_EXP) -> np.ndarray:
     return e4m3_decode(e4m3_encode(np.asarray(p, dtype=np.float64) * f)) / f
 
 
-def p_rounding_bound(qh, kh, vh, causal: bool, scale: float) -> np.ndarray:
-    """Largest |O error| that rounding P with ``round_p`` can cause, per output element.
+def _p_and_rounding_bound(qh, kh, causal: bool, scale: float):
+    """Per head: p relative to the row maximum, and b(p), the most ``round_p`` can move each p.
 
     For p * 2^k in the E4M3 normal range (>= 2^-6) rounding to nearest moves it
     by at most half a step, 2^-4 of its value (three mantissa bits); below that
-    the step is 2^-9, so p moves by at most 2^-10 / 2^k <= 2^-17 for k >= 7. With
-    l from the unrounded p, O_id = sum_j p_ij V_jd / l_i therefore moves by at
-    most sum_j b(p_ij) |V_jd| / l_i with b(p) = 2^-4 p for p >= 2^-13 and 2^-17
-    below. qh, kh, vh are the dequantized [B, H, S, D] inputs.
+    the step is 2^-9, so p moves by at most 2^-10 / 2^k <= 2^-17 for k >= 7:
+    b(p) = 2^-4 p for p >= 2^-13, 2^-17 for 0 < p < 2^-13 and 0 for p = 0.
+    Yields (bi, hi, p, b) for every head of the dequantized [B, H, S, D] inputs.
     """
-    qh, kh, vh = (np.asarray(x, dtype=np.float64) for x in (qh, kh, vh))
+    qh, kh = (np.asarray(x, dtype=np.float64) for x in (qh, kh))
     b, h, s_q, _ = qh.shape
-    s_k = kh.shape[2]
-    out = np.empty((b, h, s_q, vh.shape[3]))
-    allowed = allowed_mask(s_q, s_k, causal)
+    allowed = allowed_mask(s_q, kh.shape[2], causal)
     for bi in range(b):
         for hi in range(h):
             s = scale * (qh[bi, hi] @ kh[bi, hi].T)
             s = np.where(allowed, s, -np.inf)
             p = np.exp(s - s.max(axis=1)[:, None])
-            l = p.sum(axis=1)
             bp = np.where(p >= 2.0 ** -13, p / 16.0, np.where(p > 0, 2.0 ** -17, 0.0))
-            out[bi, hi] = (bp @ np.abs(vh[bi, hi])) / l[:, None]
+            yield bi, hi, p, bp
+
+
+def p_rounding_bound(qh, kh, vh, causal: bool, scale: float) -> np.ndarray:
+    """Largest |O error| that rounding P with ``round_p`` can cause, per output element.
+
+    With rounded weights p'_j = p_j + e_j (|e_j| <= b(p_j)) in both the sum and
+    the normaliser, O'_i - O_i = sum_j e_ij (V_jd - O_id) / l'_i, and
+    l'_i >= l_i - sum_j b(p_ij), so the error is at most
+    (sum_j b(p_ij) |V_jd| + |O_id| sum_j b(p_ij)) / (l_i - sum_j b(p_ij)).
+    Each p may be rounded with its own factor 2^k (k >= 7). qh, kh, vh are the
+    dequantized [B, H, S, D] inputs.
+    """
+    vh = np.asarray(vh, dtype=np.float64)
+    out = np.empty(tuple(np.shape(qh)[:3]) + (vh.shape[3],))
+    for bi, hi, p, bp in _p_and_rounding_bound(qh, kh, causal, scale):
+        l = p.sum(axis=1)
+        o = (p @ vh[bi, hi]) / l[:, None]
+        sb = bp.sum(axis=1)
+        out[bi, hi] = (bp @ np.abs(vh[bi, hi]) + np.abs(o) * sb[:, None]) / (l - sb)[:, None]
+    return out
+
+
+def p_rounding_lse_bound(qh, kh, causal: bool, scale: float) -> np.ndarray:
+    """Largest |LSE error| that rounding P with ``round_p`` can cause, per row ([B, H, S_q]).
+
+    The LSE is m + ln l' with l' the sum of the rounded p, and
+    |l' - l| <= sum_j b(p_j), so |ln l' - ln l| <= -ln(1 - sum_j b(p_j) / l).
+    """
+    out = np.empty(tuple(np.shape(qh)[:3]))
+    for bi, hi, p, bp in _p_and_rounding_bound(qh, kh, causal, scale):
+        out[bi, hi] = -np.log1p(-bp.sum(axis=1) / p.sum(axis=1))
     return out
 
 
@@ -128,7 +159,7 @@ def fp8_attention_sim(q, k, v, causal: bool, scale: float, scheme: str, signs=No
     quantization error, and V is never rotated, so O is directly comparable
     with exact attention on the original inputs. With ``p_quant`` the
     probabilities entering P V are ``round_p(p, p_exp)`` against the row's
-    final maximum; l and the LSE use the unrounded p.
+    final maximum, and l and the LSE are their sum.
     """
     qh, kh, vh = dequantized_inputs(q, k, v, scheme, signs, block_rows)
     b, h, s_q, d = qh.shape
@@ -156,6 +187,6 @@ def fp8_attention_rows(qh, kh, vh, rows, causal: bool, scale: float, s_q: int, p
     s = np.where(allowed_mask(s_q, kh.shape[0], causal, rows), s, -np.inf)
     m = s.max(axis=1)
     p = np.exp(s - m[:, None])
-    l = p.sum(axis=1)
     pq = round_p(p, p_exp) if p_quant else p
-    return (pq @ vh) / l[:, None], m + np.log(l)
+    lq = pq.sum(axis=1)
+    return (pq @ vh) / lq[:, None], m + np.log(lq)

@@ -466,6 +466,61 @@ def test_p_rounding_bound_holds_and_is_reached():
             assert err.max() > 0.05 * bound.max()
 
 
+def test_p_rounding_lse_bound_holds_and_is_reached():
+    """The simulated LSE (log of the sum of the rounded p) stays within the derived per-row bound for
+    every factor 2^k, k in [7, 8.75], and comes within a factor of it on some row (at k = 8.75 the
+    row's largest p, 1 * 2^8.75 = 430.5, rounds to 416 for every row)."""
+    b, h, s, d = 1, 2, 300, 64
+    q, k, v = inputs.qkv(b, h, s, s, d, seed=4, dtype=torch.bfloat16, outliers=True)
+    q, k, v = (x.float().numpy() for x in (q, k, v))
+    sg = inputs.signs(d, 4).numpy()
+    qh, kh, vh = oracle.fp8_pipeline.dequantized_inputs(q, k, v, "hadamard", sg)
+    for causal in (False, True):
+        _, ref_lse = oracle.attention(qh, kh, vh, causal, 0.125)
+        bound = oracle.p_rounding_lse_bound(qh, kh, causal, 0.125)
+        assert np.all(bound > 0) and np.all(bound < 0.07)
+        for k_exp in (7.0, 7.5, 8.0, 8.75):
+            _, lse = oracle.fp8_attention_sim(q, k, v, causal, 0.125, "hadamard", sg, p_exp=k_exp)
+            err = np.abs(lse - ref_lse)
+            assert np.all(err <= bound * (1 + 1e-9) + 1e-12), k_exp
+        assert err.max() > 0.3 * bound.max()
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_sim_constant_v_gives_constant_output(causal):
+    """Constant V gives constant O: the rounded weights are normalised by their own sum, so O is a
+    convex combination of equal rows whatever the rounding (a normaliser taken from the unrounded p
+    would leave O = c * sum(p') / sum(p), off by up to 2^-4)."""
+    q, k, _ = inputs.qkv(1, 2, 90, 130, 64, seed=6, dtype=torch.bfloat16, outliers=True)
+    q, k = q.float().numpy(), k.float().numpy()
+    v = np.full((1, 2, 130, 64), -1.75)
+    sg = inputs.signs(64, 6).numpy()
+    for k_exp in oracle.P_EXP_RANGE:
+        o, _ = oracle.fp8_attention_sim(q, k, v, causal, 0.125, "hadamard", sg, p_exp=k_exp)
+        assert np.allclose(o, -1.75, rtol=0, atol=1e-12), k_exp
+    # the other normaliser on the same rounded weights misses it
+    qh, kh, vh = oracle.fp8_pipeline.dequantized_inputs(q, k, v, "hadamard", sg)
+    sc = 0.125 * (qh[0, 0] @ kh[0, 0].T)
+    sc = np.where(oracle.allowed_mask(90, 130, causal), sc, -np.inf)
+    p = np.exp(sc - sc.max(axis=1)[:, None])
+    o_other = (oracle.round_p(p, 8.75) @ vh[0, 0]) / p.sum(axis=1)[:, None]
+    assert np.abs(o_other + 1.75).max() > 1e-3
+
+
+def test_p_rounding_lse_bound_catches_a_planted_mistake():
+    """An LSE taken from the rounded sum without undoing the 2^7 (off by 7 ln 2) breaks the bound."""
+    b, h, s, d = 1, 1, 64, 64
+    q, k, _ = inputs.qkv(b, h, s, s, d, seed=5, dtype=torch.bfloat16)
+    qh, kh = (x.float().numpy().astype(np.float64) for x in (q, k))
+    _, ref_lse = oracle.attention(qh, kh, np.zeros_like(kh), False, 0.125)
+    bound = oracle.p_rounding_lse_bound(qh, kh, False, 0.125)
+    sc = 0.125 * (qh[0, 0] @ kh[0, 0].T)
+    m = sc.max(axis=1)
+    p = np.exp(sc - m[:, None])
+    wrong = m + np.log(oracle.e4m3_decode(oracle.e4m3_encode(p * 128.0)).sum(axis=1))   # 2^7 not undone
+    assert np.all(np.abs(wrong - ref_lse[0, 0]) > bound[0, 0])
+
+
 def test_p_rounding_bound_catches_a_planted_mistake():
     """A P rounding that forgets to scale back by 2^k breaks the bound at once."""
     b, h, s, d = 1, 1, 64, 64
