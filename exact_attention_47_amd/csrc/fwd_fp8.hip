@@ -34,11 +34,18 @@
 //   next tile's scale is fetched a step ahead with a vector load: a scalar
 //   load in flight would turn every LDS wait into a full one). P is rounded
 //   to E4M3 as p * 2^7 (the factor is added to the exponent for free) so
-//   small probabilities stay out of the subnormal range; the row sum l is
-//   accumulated from the unrounded p * 2^7, and the 2^7 cancels in
-//   O = acc * vs / l. The running maximum moves whenever a row exceeds it by
-//   more than 1.75 (log2), which keeps p * 2^7 <= 430 < 448; at each move the
-//   row's largest p is exactly 2^7, which E4M3 holds without rounding.
+//   small probabilities stay out of the subnormal range. The row sum l is
+//   the sum of the rounded values, so O = acc * vs / l is the average of the
+//   V rows under the weights the product used (the 2^7 cancels) and the LSE
+//   is the log of their sum. l comes from the matrix core: one
+//   v_mfma_scale_f32_16x16x128_f8f6f4 per tile multiplies the P fragment by
+//   a selector of E4M3 ones (lane group G of A holds ones in rows r with
+//   r/4 of G's parity), which leaves in every element of output lane L the
+//   tile's sum for query L % 32 over both key halves, and takes the 32
+//   vector adds per lane and tile off the vector unit. The running maximum
+//   moves whenever a row exceeds it by more than 1.75 (log2), which keeps
+//   p * 2^7 <= 430 < 448; at each move the row's largest p is exactly 2^7,
+//   which E4M3 holds without rounding.
 //
 // * V comes as [S_k, D] codes (read transposed in flight, below) or, with
 //   v_transposed, as [D, S_k] codes: those tiles are stored [128 d][64 keys]
@@ -85,6 +92,11 @@ __device__ __forceinline__ int v8_swz(int r) { return 2 * (((r >> 1) & 1) | ((r 
 
 __device__ __forceinline__ v16f mma8(v8i a, v8i b, v16f c) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+// the same product with a 16x16 output: the P tile's row sums (above)
+__device__ __forceinline__ v4f mma8_rows(v8i a, v8i b, v4f c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
 
 __device__ __forceinline__ uint32_t pack_fp8(float a, float b, float c, float d) {
@@ -244,6 +256,16 @@ fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ K8, c
 #pragma unroll
     for (int e = 0; e < 16; e++) o[db][e] = 0.0f;
   float m = kNegInf, l = 0.0f, rf = 0.0f;
+  // A operand of the row-sum product: lane (G = lane / 16, r = lane % 16)
+  // holds E4M3 ones (0x38) when G and r / 4 have the same parity. B lane
+  // 16 G + n holds query n + 16 (G % 2), key half G / 2, so output row r
+  // (lanes G' = r / 4) sums the two B lane groups of its query
+  v8i ones_sel;
+  {
+    const int sel = ((lane >> 4) & 1) == ((lane >> 2) & 1) ? 0x38383838 : 0;
+#pragma unroll
+    for (int i = 0; i < 8; i++) ones_sel[i] = sel;
+  }
 
   const __amdgpu_buffer_rsrc_t ksrs = __builtin_amdgcn_make_buffer_rsrc((void*)ksh, (short)0, nk_blk * 4, 0x00020000);
   auto tile_scale_v = [&](int t) {
@@ -340,11 +362,11 @@ fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ K8, c
 #pragma unroll
       for (int e = 0; e < 4; e++) {
         p[e] = fast_exp2(__builtin_fmaf(s[b][4 * q4 + e], cc, nref));
-        l += p[e];
       }
       pf[quad] = (int)pack_fp8(p[0], p[1], p[2], p[3]);
     }
-    // O^T += V^T P^T: four 32x32x64 steps, one per 32-row block of O^T
+    // O^T += V^T P^T: four 32x32x64 steps, one per 32-row block of O^T, and
+    // the tile's row sums (issued first: they need no LDS read)
     {
       const char* vl = rbuf + TILE8;
       auto load = [&](int db) {
@@ -366,11 +388,14 @@ fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ K8, c
       };
       v8i ring[2];
       ring[0] = load(0);
+      const v4f zero4 = {};
+      const v4f lt = mma8_rows(ones_sel, pf, zero4);
 #pragma unroll
       for (int db = 0; db < DB8; db++) {
         if (db + 1 < DB8) ring[(db + 1) & 1] = load(db + 1);
         o[db] = mma8(ring[db & 1], pf, o[db]);
       }
+      l += lt[0];
     }
     cs_cur = c_nx;
     __builtin_amdgcn_s_waitcnt(0x0070 | 0x0F00 | (2 * NI8 + 1));   // stage t+1 complete
@@ -417,7 +442,7 @@ fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ K8, c
 
   // epilogue: O = acc * vs / l (the 2^7 of p cancels), LSE = ln2 * (m + log2 l - 7)
   const int q = wr0 + nn;
-  const float lt = pair_sum(l);
+  const float lt = l;                           // the whole row's sum in both halves
   const bool has = m != kNegInf && lt > 0.0f;
   const float inv = has ? v_scale / lt : 0.0f;
   const float lse = has ? (m + __builtin_log2f(lt) - kPShift8) * kLn2 : kNegInf;

@@ -5,11 +5,14 @@
 * attn_fwd_fp8: against exact float64 attention on the dequantized inputs
   (the oracle's own quantization, which the first tests prove identical to the
   kernel's). The only approximations left in the kernel are P rounded to E4M3
-  (relative to a running reference), bf16 output and float32 accumulation:
-  every element stays within the bound that rounding P can cause
-  (oracle.p_rounding_bound) plus half a bf16 step, and the RMSE within 15 % of
-  the simulated P-rounding envelope. On inputs where every probability is an
-  exact power of two the kernel must match to half a bf16 step.
+  (relative to a running reference; the row sum is the sum of the rounded
+  values), bf16 output and float32 accumulation: every element stays within
+  the bound that rounding P can cause (oracle.p_rounding_bound) plus half a
+  bf16 step, every LSE within oracle.p_rounding_lse_bound, and the RMSE within
+  15 % of the simulated P-rounding envelope. On inputs where every probability
+  is an exact power of two the kernel must match to half a bf16 step, and a
+  constant V must come out unchanged (the weights are normalised by their own
+  sum).
 * The pages' claim on the configured workload (B=2, H=16, S=8K, D=128,
   N(0,1) with 0.1 % outliers): FP8 with the random-sign Hadamard transform and
   64-row block scales has at most half the RMSE of plain per-tensor FP8,
@@ -139,11 +142,11 @@ def test_fp8_attention_against_dequantized_oracle(gpu_lib, S_q, S_k, causal):
 
     What is left is P rounded to E4M3 (p * 2^k, k between 7 and 8.75 relative to the row's final
     maximum), bf16 rounding of O and float32 accumulation:
-      * per element: |error| <= oracle.p_rounding_bound (half an E4M3 step of every p, times |V|, over l)
-        + half a bf16 step of O (2^-8 relative) + float32 slack;
+      * per element: |error| <= oracle.p_rounding_bound (half an E4M3 step of every p, against |V| and
+        |O|, over the rounded l) + half a bf16 step of O (2^-8 relative) + float32 slack;
       * RMSE within +-15 % of the simulated P-rounding envelope (oracle.fp8_attention_sim at k = 7 and
         k = 8.75, the ends of the kernel's factor against the row's final maximum);
-      * LSE uses the unrounded p: float32 error only.
+      * LSE = the log of the rounded row sum: within oracle.p_rounding_lse_bound per row + float32 slack.
     """
     note(f"fp8 attention S_q{S_q} S_k{S_k} causal={causal}")
     B, H, D = 1, 2, 128
@@ -161,13 +164,34 @@ def test_fp8_attention_against_dequantized_oracle(gpu_lib, S_q, S_k, causal):
     limit = bound * (1 + 1e-2) + 2.0 ** -8 * (np.abs(ref) + bound) + 1e-6
     env = p_envelope(qf, kf, vf, causal, scale, sn, ref)
     rm = float(np.sqrt(np.mean(err ** 2)))
-    lse_err = float(np.abs(lse.cpu().numpy() - ref_lse).max())
+    lse_abs = np.abs(lse.cpu().numpy() - ref_lse)
+    lse_lim = oracle.p_rounding_lse_bound(qh, kh, causal, scale) * (1 + 1e-2) + 1e-5
     print(f"    fp8: O rmse {rm:.3e} (P-rounding sim k=7 {env[0]:.3e}, k=8.75 {env[1]:.3e}) "
           f"max {err.max():.3e}, largest error / per-element limit {float((err / limit).max()):.3f}, "
-          f"LSE max {lse_err:.3e}", flush=True)
+          f"LSE max {lse_abs.max():.3e} (largest / per-row limit {float((lse_abs / lse_lim).max()):.3f})",
+          flush=True)
     assert np.all(err <= limit)
     assert 0.85 * min(env) <= rm <= 1.15 * max(env)
-    assert lse_err <= 1e-3
+    assert np.all(lse_abs <= lse_lim)
+
+
+@pytest.mark.parametrize("S_q,S_k,causal", [(300, 700, False), (520, 520, True), (130, 61, False),
+                                            (2100, 2100, True)])
+def test_fp8_attention_constant_v(gpu_lib, S_q, S_k, causal):
+    """Constant V gives constant O: the kernel divides by the sum of the same rounded weights that
+    multiply V, so O = c up to float32 accumulation and the bf16 rounding of O, on any scores (here
+    the outlier workload's, on ragged tiles and the causal diagonal)."""
+    note(f"fp8 constant V S_q{S_q} S_k{S_k} causal={causal}")
+    B, H, D = 1, 2, 128
+    scale = 1 / math.sqrt(D)
+    q, k, _ = inputs.qkv(B, H, S_q, S_k, D, seed=11, dtype=torch.bfloat16, outliers=True)
+    v = torch.full((B, H, S_k, D), -1.75, dtype=torch.bfloat16)
+    sg = inputs.signs(D, 11)
+    o, _ = _pipeline(gpu_lib, q.cuda(), k.cuda(), v.cuda(), sg.cuda(), causal, scale)
+    torch.cuda.synchronize()
+    err = float((o.float().cpu() + 1.75).abs().max())
+    print(f"    fp8 constant V: max |O - c| {err:.3e}", flush=True)
+    assert err <= 1.75 * 2.0 ** -8
 
 
 # fl32(ln 2): its float32 product with fl32(log2 e), the factor the library folds into the exponent,
