@@ -322,8 +322,9 @@ int quant_per_tensor(const void* x, void* x8, float* scale, int B, int H, int S,
  * Scores are scale * (q8 . k8) * q_scale(row block) * k_scale(key block).
  * The probabilities entering P V are rounded to E4M3 after multiplication by
  * 2^7 (relative to the row's running reference, which moves when the row
- * grows by more than 1.75 in log2); the row sums use the unrounded values.
- * D = 128.
+ * grows by more than 1.75 in log2); the row sums are those of the rounded
+ * values, so O is normalised by the weights that multiply V and the LSE is the
+ * log of their sum. D = 128.
  */
 int attn_fwd_fp8(const void* q8, const void* k8, const void* v8,
                  const float* q_scales, const float* k_scales, const float* v_scale,
