@@ -325,7 +325,7 @@ int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float*
   else if (dtype != ATTN_F32 && dtype != ATTN_F16 && dtype != ATTN_BF16) rc = ATTN_ERR_INVALID_ARG;
   else if (causal != 0 && causal != 1) rc = ATTN_ERR_INVALID_ARG;
   else if (!(scale > 0.0f) || !isfinite(scale)) rc = ATTN_ERR_INVALID_ARG;
-  else if (dtype == ATTN_F32 || (D != 64 && D != 128)) rc = ATTN_ERR_UNSUPPORTED;
+  else if (dtype == ATTN_F32 || (D != 64 && D != 128 && D != 256)) rc = ATTN_ERR_UNSUPPORTED;
   else if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4) ||
            !aligned(cu_seqlens_q, 4) || !aligned(cu_seqlens_k, 4))
     rc = ATTN_ERR_MISALIGNED;

@@ -21,6 +21,10 @@
 // bytes) touch every bank of the 64-bank LDS once. Rows past the end of K/V
 // read zeros (their scores are masked): the tile that reaches past the end
 // is loaded with range-checked offsets.
+//
+// Packed batches (VARLEN): [total, H, D] rows H*D elements apart, each
+// workgroup looking up its sequence's offsets; the load offsets step by that
+// row pitch and the buffer range ends after the sequence's last row.
 #include "common.h"
 #include "kernels.h"
 
@@ -63,14 +67,16 @@ struct Cfg256 {
 
 constexpr float kTau256 = 8.0f;   // lazy-rescale threshold, log2 domain
 
-template <typename T, int D, int QB, int NW, int BN, bool CAUSAL, bool SPLIT>
+template <typename T, int D, int QB, int NW, int BN, bool CAUSAL, bool SPLIT, bool VARLEN>
 __global__ void __launch_bounds__(NW * 64)
 __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
 fwd_d256_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
                 T* __restrict__ O, float* __restrict__ LSE,
                 float* __restrict__ Opart, float* __restrict__ Lpart,
-                int BH, int S_q, int S_k, int n_qt, int n_split, int keys_per_split, float c)
+                int BH, int S_q_, int S_k_, int n_qt, int n_split, int keys_per_split, float c,
+                const int* __restrict__ cu_q, const int* __restrict__ cu_k, int H, int total_q)
 {
+  static_assert(!(VARLEN && SPLIT), "packed batches run unsplit");
   using C = Cfg256<D, QB, NW, BN>;
   using M = Mma256<T>;
   typedef typename M::frag frag;
@@ -85,7 +91,20 @@ fwd_d256_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
 
   // ---- which (b*h, q tile, split) this workgroup computes
   int split = 0, qt, bh;
-  if (CAUSAL && !SPLIT && n_qt >= 16) {
+  if (VARLEN) {
+    // packed batches: XCD x takes heads x, x+8, ... one at a time with all
+    // their query tiles (highest first) when B*H is a multiple of 8, so a
+    // head's K and V stay in one L2; otherwise query tiles heaviest first
+    // over all heads
+    if (BH % 8 == 0) {
+      const int x = blockIdx.x % 8, j = blockIdx.x / 8;
+      bh = x + 8 * (j / n_qt);
+      qt = n_qt - 1 - j % n_qt;
+    } else {
+      qt = n_qt - 1 - (int)(blockIdx.x / BH);
+      bh = blockIdx.x % BH;
+    }
+  } else if (CAUSAL && !SPLIT && n_qt >= 16) {
     // query tiles heaviest first over all (b, h) at a time; consecutive
     // workgroups go to the 8 XCDs in turn, so (b, h) stays on XCD bh % 8
     // when B*H is a multiple of 8
@@ -103,6 +122,35 @@ fwd_d256_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
 
   const int q0 = qt * C::BM;
   const int wr0 = q0 + wave * C::RPW;          // first row of this wave
+
+  // ---- where this (b, h) lives. Dense: [B, H, S, D], rows D elements apart.
+  // Packed ([GN] "Weitere Optimierungen und kuenftige Integration" names
+  // variable-length sequences): [total, H, D], sequence b at rows
+  // cu[b] .. cu[b+1]-1, rows H*D elements apart; LSE is [H, total_q].
+  int S_q = S_q_, S_k = S_k_;
+  const int pitch = VARLEN ? H * D : D;        // elements between consecutive rows
+  const T *Qh, *Kh, *Vh;
+  T* Oh;
+  float* lseh;
+  if (VARLEN) {
+    const int b = bh / H, h = bh % H;
+    const int q_beg = cu_q[b], k_beg = cu_k[b];
+    S_q = cu_q[b + 1] - q_beg;
+    S_k = cu_k[b + 1] - k_beg;
+    if (q0 >= S_q) return;                     // whole workgroup: past this sequence's rows
+    Qh = Q + ((size_t)q_beg * H + h) * D;
+    Kh = K + ((size_t)k_beg * H + h) * D;
+    Vh = V + ((size_t)k_beg * H + h) * D;
+    Oh = O + ((size_t)q_beg * H + h) * D;
+    lseh = LSE + (size_t)h * total_q + q_beg;
+  } else {
+    Qh = Q + (size_t)bh * S_q * D;
+    Kh = K + (size_t)bh * S_k * D;
+    Vh = V + (size_t)bh * S_k * D;
+    Oh = O + (size_t)bh * S_q * D;
+    lseh = LSE + (size_t)bh * S_q;
+  }
+  const int RBg = pitch * (int)sizeof(T);      // bytes between consecutive rows in memory
   const int diag = S_k - S_q;                  // causal: key j allowed iff j <= i + diag
   int k_lo = 0, k_hi = S_k;
   if (SPLIT) {
@@ -113,12 +161,6 @@ fwd_d256_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
   if (CAUSAL) k_end = min(k_end, q0 + C::BM - 1 + diag + 1);
   const int n_tiles = k_end > k_lo ? (k_end - k_lo + C::BN - 1) / C::BN : 0;
 
-  const size_t qoff = (size_t)bh * S_q * D;
-  const size_t koff = (size_t)bh * S_k * D;
-  const T* Qh = Q + qoff;
-  const T* Kh = K + koff;
-  const T* Vh = V + koff;
-
   // ---- Q^T fragments (B operand of S^T), kept in registers
   frag qf[QB][C::DS];
 #pragma unroll
@@ -127,7 +169,7 @@ fwd_d256_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
 #pragma unroll
     for (int ds = 0; ds < C::DS; ds++) {
       if (q < S_q) {
-        qf[qb][ds] = *(const frag*)(Qh + (size_t)q * D + ds * 16 + 8 * hh);
+        qf[qb][ds] = *(const frag*)(Qh + (size_t)q * pitch + ds * 16 + 8 * hh);
       } else {
 #pragma unroll
         for (int e = 0; e < 8; e++) qf[qb][ds][e] = (T)0.0f;
@@ -137,16 +179,19 @@ fwd_d256_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
 
   // ---- direct loads of one K/V tile: per-head buffer resources, one
   // lane-constant offset (a lane's rows step by a multiple of 16 between its
-  // loads, which leaves both swizzles unchanged) plus wave-uniform scalars
-  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)Kh, (short)0, S_k * C::RB, 0x00020000);
-  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)Vh, (short)0, S_k * C::RB, 0x00020000);
+  // loads, which leaves both swizzles unchanged) plus wave-uniform scalars.
+  // The range ends after the last row (packed rows are RBg bytes apart), so
+  // rows past it read zeros.
+  const int kv_bytes = VARLEN ? (S_k > 0 ? (S_k - 1) * RBg + C::RB : 0) : S_k * C::RB;
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)Kh, (short)0, kv_bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)Vh, (short)0, kv_bytes, 0x00020000);
   int lane_k, lane_v;
   {
     const int rsub = (lane * 16) / C::RB;
     const int u = ((lane * 16) % C::RB) / 16;
     const int r = wave * C::RPI + rsub;
-    lane_k = rsub * C::RB + ((u ^ (r & 15)) * 16);
-    lane_v = rsub * C::RB + ((u ^ (4 * (r & 3))) * 16);
+    lane_k = rsub * RBg + ((u ^ (r & 15)) * 16);
+    lane_v = rsub * RBg + ((u ^ (4 * (r & 3))) * 16);
   }
   // (offsets and destinations go through locals: a target builtin with
   // template-dependent argument expressions is dropped from the host pass)
@@ -160,7 +205,7 @@ fwd_d256_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
         const int blk = i * C::NW + wave;
         char* kdst = base + blk * 1024;
         char* vdst = base + C::TILE + blk * 1024;
-        const int soff = key0 * C::RB + blk * 1024;
+        const int soff = (key0 + blk * C::RPI) * RBg;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (__attribute__((address_space(3))) void*)kdst, 16, lane_k,
                                                  soff, 0, 0);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (__attribute__((address_space(3))) void*)vdst, 16, lane_v,
@@ -172,8 +217,8 @@ fwd_d256_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
         const int blk = i * C::NW + wave;
         char* kdst = base + blk * 1024;
         char* vdst = base + C::TILE + blk * 1024;
-        const int koff = lane_k + key0 * C::RB + blk * 1024;
-        const int voff = lane_v + key0 * C::RB + blk * 1024;
+        const int koff = lane_k + (key0 + blk * C::RPI) * RBg;
+        const int voff = lane_v + (key0 + blk * C::RPI) * RBg;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (__attribute__((address_space(3))) void*)kdst, 16, koff,
                                                  0, 0, 0);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (__attribute__((address_space(3))) void*)vdst, 16, voff,
@@ -348,7 +393,7 @@ fwd_d256_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
     const float lse = has ? (m[qb] + __builtin_log2f(lt)) * kLn2 : kNegInf;
     if (q < S_q) {
       if (!SPLIT) {
-        T* orow = O + qoff + (size_t)q * D;
+        T* orow = Oh + (size_t)q * pitch;
 #pragma unroll
         for (int db = 0; db < C::DB; db++)
 #pragma unroll
@@ -359,7 +404,7 @@ fwd_d256_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
             for (int j = 0; j < 4; j++) w[j] = (T)(o[qb][db][4 * i + j] * inv);
             *(v4t*)(orow + db * 32 + 8 * i + 4 * hh) = w;
           }
-        if (hh == 0) LSE[(size_t)bh * S_q + q] = lse;
+        if (hh == 0) lseh[q] = lse;
       } else {
         const size_t prow = ((size_t)split * BH + bh) * S_q + q;
         float* orow = Opart + prow * D;
@@ -392,9 +437,24 @@ static hipError_t launch_256(const FwdArgs& a, hipStream_t st) {
   if ((long long)(a.S_k + C::BN) * C::RB > 0x7fffffffLL) return hipErrorInvalidValue;   // 32-bit buffer offsets
   const int n_qt = (a.S_q + C::BM - 1) / C::BM;
   const int n_work = a.B * a.H * n_qt * a.n_split;
-  hipLaunchKernelGGL((fwd_d256_kernel<T, 256, 1, 8, D256_BN, CAUSAL, SPLIT>), dim3(n_work), dim3(C::NT), 0, st,
-                     (const T*)a.q, (const T*)a.k, (const T*)a.v, (T*)a.o, a.lse, a.opart, a.lpart,
-                     a.B * a.H, a.S_q, a.S_k, n_qt, a.n_split, a.keys_per_split, a.c);
+  hipLaunchKernelGGL((fwd_d256_kernel<T, 256, 1, 8, D256_BN, CAUSAL, SPLIT, false>), dim3(n_work), dim3(C::NT), 0,
+                     st, (const T*)a.q, (const T*)a.k, (const T*)a.v, (T*)a.o, a.lse, a.opart, a.lpart,
+                     a.B * a.H, a.S_q, a.S_k, n_qt, a.n_split, a.keys_per_split, a.c, nullptr, nullptr, a.H, 0);
+  return hipGetLastError();
+}
+
+// packed batches: S_q / S_k are the longest sequences; the grid covers
+// B*H*ceil(S_q / 256) workgroups, and those past their sequence exit at once
+template <typename T, bool CAUSAL>
+static hipError_t launch_256_varlen(const FwdArgs& a, hipStream_t st) {
+  using C = Cfg256<256, 1, 8, D256_BN>;
+  // 32-bit buffer offsets over H*D-element row steps
+  if ((long long)(a.S_k + C::BN) * a.H * C::RB > 0x7fffffffLL) return hipErrorInvalidValue;
+  const int n_qt = (a.S_q + C::BM - 1) / C::BM;
+  const int n_work = a.B * a.H * n_qt;
+  hipLaunchKernelGGL((fwd_d256_kernel<T, 256, 1, 8, D256_BN, CAUSAL, false, true>), dim3(n_work), dim3(C::NT), 0,
+                     st, (const T*)a.q, (const T*)a.k, (const T*)a.v, (T*)a.o, a.lse, nullptr, nullptr,
+                     a.B * a.H, a.S_q, a.S_k, n_qt, 1, 0, a.c, a.cu_q, a.cu_k, a.H, a.total_q);
   return hipGetLastError();
 }
 
@@ -410,6 +470,12 @@ int d256_keys_per_tile() { return D256_BN; }
 hipError_t launch_fwd_d256(const FwdArgs& a, hipStream_t st) {
   if (a.dtype == 2) return launch_256_t<__bf16>(a, st);
   return launch_256_t<_Float16>(a, st);
+}
+
+hipError_t launch_fwd_d256_varlen(const FwdArgs& a, hipStream_t st) {
+  if (a.dtype == 2)
+    return a.causal ? launch_256_varlen<__bf16, true>(a, st) : launch_256_varlen<__bf16, false>(a, st);
+  return a.causal ? launch_256_varlen<_Float16, true>(a, st) : launch_256_varlen<_Float16, false>(a, st);
 }
 
 }  // namespace attn

@@ -174,8 +174,11 @@ int attn_fwd_persistent(const void* q, const void* k, const void* v, void* o, fl
  *
  * A query row with no allowed key (an empty key sequence, or causal rows
  * above the diagonal when S_q > S_k) gets O = 0 and LSE = -inf. Empty query
- * sequences write nothing. dtype is ATTN_BF16 or ATTN_F16 (ATTN_F32 and D =
- * 256 return ATTN_ERR_UNSUPPORTED); D is 64 or 128. q, k, v, o must be
+ * sequences write nothing. dtype is ATTN_BF16 or ATTN_F16 (ATTN_F32 returns
+ * ATTN_ERR_UNSUPPORTED); D is 64, 128 or 256 (others ATTN_ERR_UNSUPPORTED;
+ * so is a longest key sequence whose rows span 2^31 bytes or more of K,
+ * (max_seqlen_k + 128) * H * D * 2 at D = 64 / 128 and (max_seqlen_k + 32) *
+ * H * 512 at D = 256). q, k, v, o must be
  * 16-byte aligned, lse and the cu arrays 4-byte aligned; q, o, lse may be
  * NULL when total_q = 0 and k, v when total_k = 0. total_q = 0 returns
  * ATTN_OK without launching.

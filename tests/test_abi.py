@@ -126,8 +126,11 @@ def varlen(**kw):
     (dict(causal=3), attn.ERR_INVALID_ARG),
     (dict(scale=-1.0), attn.ERR_INVALID_ARG),
     (dict(dtype=0), attn.ERR_UNSUPPORTED),
-    (dict(D=256), attn.ERR_UNSUPPORTED),
+    (dict(D=192), attn.ERR_UNSUPPORTED),
     (dict(D=96), attn.ERR_UNSUPPORTED),
+    # D = 256: K rows of the longest sequence span (2.1M + 32) * H * 512 bytes >= 2^31, past the
+    # kernel's 32-bit buffer offsets (refused on the host before any launch)
+    (dict(D=256, total_k=3_000_000, max_k=2_100_000), attn.ERR_UNSUPPORTED),
     (dict(q=P + 8), attn.ERR_MISALIGNED),
     (dict(cu_k=P + 2), attn.ERR_MISALIGNED),
 ])

@@ -54,7 +54,7 @@ CASES = [
 ]
 
 
-@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("D", [64, 128, 256])
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
 @pytest.mark.parametrize("case", range(len(CASES)))
 def test_varlen_against_oracle(gpu_lib, case, dtype, D):
@@ -67,14 +67,16 @@ def test_varlen_against_oracle(gpu_lib, case, dtype, D):
     check(o, lse, q, k, v, cu_q, cu_k, causal, scale, f"case {case}")
 
 
-@pytest.mark.parametrize("S,causal", [(2000, False), (2500, True)])
-def test_varlen_equal_lengths_bitwise_equal_dense(gpu_lib, S, causal):
+@pytest.mark.parametrize("S,causal,D", [(2000, False, 128), (2500, True, 128), (700, False, 256),
+                                        (1100, True, 256)])
+def test_varlen_equal_lengths_bitwise_equal_dense(gpu_lib, S, causal, D):
     """B sequences of one length: the packed path gives the dense path's bits, transposed in layout.
 
-    (Lengths where the dense entry point also runs the main kernel: shorter ranges go to the
-    short-range kernel, whose different tiling changes the rounding order.)"""
-    note(f"varlen vs dense S{S} causal={causal}")
-    B, H, D = 2, 4, 128
+    (Lengths where the dense entry point runs the same kernel unsplit: the main kernel at D = 128
+    beyond the short-range kernel's ranges, whose different tiling changes the rounding order, and
+    the D = 256 kernel at any length here.)"""
+    note(f"varlen vs dense S{S} causal={causal} D{D}")
+    B, H = 2, 4
     q, k, v = inputs.qkv(B, H, S, S, D, seed=5, dtype=torch.bfloat16, device="cuda")
     o_d, lse_d = gpu_lib.fwd(q, k, v, causal=causal)
     pack = lambda t: t.transpose(1, 2).reshape(B * S, H, D).contiguous()
@@ -85,12 +87,13 @@ def test_varlen_equal_lengths_bitwise_equal_dense(gpu_lib, S, causal):
     assert torch.equal(lse_v, lse_d.permute(1, 0, 2).reshape(H, B * S))
 
 
-def test_varlen_fullsize_sampled_rows(gpu_lib):
+@pytest.mark.parametrize("H,D", [(16, 128), (8, 256)])
+def test_varlen_fullsize_sampled_rows(gpu_lib, H, D):
     """The bench workload (8 causal sequences of random lengths summing to 16K tokens, H16 D128)
-    launched as the bench launches it; sampled rows of every sequence against the oracle."""
+    launched as the bench launches it, and the same lengths at D = 256 (H8, the D = 256 shape's
+    heads); sampled rows of every sequence against the oracle."""
     lens = inputs.sequence_lengths(8, 16384, 0, 256)
-    note(f"varlen full size lens={lens} H16 D128 causal")
-    H, D = 16, 128
+    note(f"varlen full size lens={lens} H{H} D{D} causal")
     scale = D ** -0.5
     q, k, v, cu_q, cu_k = inputs.packed_qkv(lens, lens, H, D, seed=0, device="cuda")
     o, lse = gpu_lib.fwd_varlen(q, k, v, cu_q, cu_k, causal=True, scale=scale)
