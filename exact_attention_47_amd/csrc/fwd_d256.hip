@@ -85,7 +85,7 @@ fwd_d256_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar offsets)
   const int hh = lane >> 5;        // lane half
   const int nn = lane & 31;        // query column owned by this lane
 
