@@ -291,7 +291,7 @@ int rope_hadamard_quant(const void* x, void* x8, float* scales, const signed cha
  * (four small launches on `stream`: clear, max |x|, quantize, final scale).
  * Used for V on the FP8 path and for the plain per-tensor FP8 baseline
  * without a transform: the pages compare incoherent processing against FP8
- * "without transformations" and report the error ratio ([NL] "3. Lage
+ * with no transform applied and report the error ratio ([NL] "3. Lage
  * precisie (FP8) met reductie van kwantisatiefout"; [GN] "Niedrige
  * FP8-Praezision und incoherent processing").
  *

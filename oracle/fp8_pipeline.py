@@ -10,8 +10,8 @@ reductie van kwantisatiefout"; [GN] "Niedrige FP8-Präzision und incoherent
 processing"). This module simulates both schemes so that the expected error of
 each, and their ratio, can be computed on the CPU.
 
-Schemes (the plain per-tensor baseline is the pages' "FP8 without
-transformations"):
+Schemes (the plain per-tensor baseline is the pages' FP8 comparison with no
+transform applied):
 
 * ``"hadamard"``: Q, K -> random-sign Hadamard, then per-``block_rows`` block
   scales (``oracle.fp8.hadamard_quantize``); V -> one per-tensor scale.
