@@ -611,7 +611,6 @@ hipError_t launch_fwd_mfma(const FwdArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_fwd_varlen(const FwdArgs& a, hipStream_t st) {
-  if (a.D == 256) return launch_fwd_d256_varlen(a, st);
   if (a.dtype == 2) return launch_varlen_t<__bf16>(a, st);
   return launch_varlen_t<_Float16>(a, st);
 }

@@ -64,7 +64,7 @@ hipError_t launch_fwd_short(const FwdArgs& a, hipStream_t st);
 int short_rows_per_block();
 int short_keys_per_tile();
 
-// head dimension 256 (called through launch_fwd_mfma / launch_fwd_varlen)
+// head dimension 256 (dense: called through launch_fwd_mfma; packed: from attn_fwd_varlen)
 hipError_t launch_fwd_d256(const FwdArgs& a, hipStream_t st);
 hipError_t launch_fwd_d256_varlen(const FwdArgs& a, hipStream_t st);
 int d256_keys_per_tile();
