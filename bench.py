@@ -164,10 +164,10 @@ def decode_point(steps=10, warmup=3):
     return res
 
 
-def varlen_point(causal=True, steps=10, warmup=3):
-    """Packed batch: 8 sequences of random lengths (>= 256) summing to 16K tokens, H=16, D=128, bf16."""
+def varlen_point(causal=True, steps=10, warmup=3, H=16, D=128):
+    """Packed batch: 8 sequences of random lengths (>= 256) summing to 16K tokens, by default H=16, D=128, bf16
+    (H=8, D=256 is the D = 256 kernel's packed form on the same lengths)."""
     lens = inputs.sequence_lengths(8, 16384, 0, 256)
-    H, D = 16, 128
     q, k, v, cu_q, cu_k = inputs.packed_qkv(lens, lens, H, D, seed=0, device="cuda")
     o = torch.empty_like(q)
     lse = torch.empty((H, q.shape[0]), dtype=torch.float32, device="cuda")
@@ -349,7 +349,8 @@ def main():
                                      for n in (512, 1024, 2048, 4096, 8192, 16384)],
             "d64_sweep": lambda: [bf16_point(16384 // n, 32, n, n, 64, False, steps=st, warmup=wu)
                                   for n in (512, 1024, 2048, 4096, 8192, 16384)],
-            "varlen": lambda: [varlen_point(c, steps=st, warmup=wu) for c in (True, False)],
+            "varlen": lambda: [varlen_point(c, steps=st, warmup=wu, H=h, D=d) for h, d in ((16, 128), (8, 256))
+                               for c in (True, False)],
             "bwd": lambda: [bwd_point(c, steps=st, warmup=wu) for c in (False, True)],
             "bwd_d64": lambda: [bwd_point(c, B=4, H=32, S=4096, D=64, steps=st, warmup=wu) for c in (False, True)],
             "persistent": lambda: persistent_points(steps=st, warmup=wu),
@@ -433,7 +434,8 @@ def main():
         extras["causal_d256_8k"] = bf16_point(2, 8, 8192, 8192, 256, True)
         extras["decode_32k"] = decode_point()
         extras["fp8_pipeline_8k"] = fp8_point()
-        extras["varlen_16k_tokens"] = [varlen_point(True), varlen_point(False)]
+        extras["varlen_16k_tokens"] = [varlen_point(c, H=h, D=d) for h, d in ((16, 128), (8, 256))
+                                       for c in (True, False)]
         extras["backward_8k"] = [bwd_point(False), bwd_point(True)]
         # D = 64 runs dK and dV in one pass (S and P once for both)
         extras["backward_d64_4k"] = [bwd_point(False, B=4, H=32, S=4096, D=64),
