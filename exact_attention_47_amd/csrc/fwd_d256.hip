@@ -197,7 +197,10 @@ fwd_d256_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
   // template-dependent argument expressions is dropped from the host pass)
   // The buffer range check covers the per-lane offset and not the scalar
   // one: a tile that reaches past the last row puts its whole offset in the
-  // per-lane part, so that its rows past the end read zeros.
+  // per-lane part (dense), or gets one resource per instruction based at the
+  // instruction's first row with the bytes left after it as its range
+  // (packed, where the per-lane offsets spilled), so that its rows past the
+  // end read zeros.
   auto issue_tile = [&](int key0, char* base) {
     if (key0 + C::BN <= S_k) {
 #pragma unroll
@@ -217,12 +220,25 @@ fwd_d256_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
         const int blk = i * C::NW + wave;
         char* kdst = base + blk * 1024;
         char* vdst = base + C::TILE + blk * 1024;
-        const int koff = lane_k + (key0 + blk * C::RPI) * RBg;
-        const int voff = lane_v + (key0 + blk * C::RPI) * RBg;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (__attribute__((address_space(3))) void*)kdst, 16, koff,
-                                                 0, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (__attribute__((address_space(3))) void*)vdst, 16, voff,
-                                                 0, 0, 0);
+        if constexpr (VARLEN) {
+          const int off = (key0 + blk * C::RPI) * RBg;
+          const int left = kv_bytes > off ? kv_bytes - off : 0;
+          const __amdgpu_buffer_rsrc_t k1 =
+              __builtin_amdgcn_make_buffer_rsrc((void*)((const char*)Kh + off), (short)0, left, 0x00020000);
+          const __amdgpu_buffer_rsrc_t v1 =
+              __builtin_amdgcn_make_buffer_rsrc((void*)((const char*)Vh + off), (short)0, left, 0x00020000);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(k1, (__attribute__((address_space(3))) void*)kdst, 16, lane_k,
+                                                   0, 0, 0);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(v1, (__attribute__((address_space(3))) void*)vdst, 16, lane_v,
+                                                   0, 0, 0);
+        } else {
+          const int koff = lane_k + (key0 + blk * C::RPI) * RBg;
+          const int voff = lane_v + (key0 + blk * C::RPI) * RBg;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (__attribute__((address_space(3))) void*)kdst, 16, koff,
+                                                   0, 0, 0);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (__attribute__((address_space(3))) void*)vdst, 16, voff,
+                                                   0, 0, 0);
+        }
       }
     }
   };
