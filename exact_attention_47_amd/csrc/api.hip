@@ -65,13 +65,24 @@ size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 // at 1024, +4.5 % at 2048, -1.4 % at 4096), causal D = 64 up to 8192 (+9 % at
 // 2048, +14 % at 4096, +5.6 % at 8192, equal at 16384), D = 128 causal up to
 // 2048 (+20 % at 512, +2.6 % at 1024, +1.4 % at 2048, equal at 4096), D = 128
-// non-causal up to 1024 (+13 % at 512, +2.4 % at 1024). Requested splits
-// always go to the main kernel, whose key tile the split plan uses.
+// non-causal up to 1024 (+13 % at 512, +2.4 % at 1024). Key-range splits go
+// to the main kernel, whose key tile the split plan uses, except those of
+// short query blocks (use_short_split).
 bool use_short_kernel(int D, int causal, int S_k, int n_split) {
   if (n_split != 1) return false;
   if (D == 64) return S_k <= (causal ? 8192 : 4096);
   if (D == 128) return S_k <= (causal ? 2048 : 1024);
   return false;
+}
+
+// A key-range split of a short query block (more than the decode kernel's one
+// row, at most one short-range workgroup's rows) runs on the short-range
+// kernel: its 128-row workgroups carry half the main kernel's idle rows, and
+// the main kernel's 256 rows of matrix work per key tile then no longer stand
+// beside the K/V stream. (The split plan's key granularity, the main kernel's
+// 128-key tile, is a multiple of the short-range kernel's 32-key tile.)
+bool use_short_split(int D, int S_q, int n_split) {
+  return n_split > 1 && (D == 64 || D == 128) && S_q <= attn::short_rows_per_block();
 }
 
 // Causal D = 128 on the main kernel runs on the persistent grid: its snake
@@ -150,7 +161,8 @@ int run_fwd(const void* q, const void* k, const void* v, void* o, float* lse, in
   int n_cu = 0;
   if (dtype == ATTN_F32) e = attn::launch_fwd_f32(a, st);
   else if (p.n_split > 1 && S_q <= attn::decode_max_rows()) e = attn::launch_fwd_decode(a, st);
-  else if (use_short_kernel(D, causal, S_k, p.n_split)) e = attn::launch_fwd_short(a, st);
+  else if (use_short_kernel(D, causal, S_k, p.n_split) || use_short_split(D, S_q, p.n_split))
+    e = attn::launch_fwd_short(a, st);
   else if (use_persistent(D, causal, p.n_split) && (n_cu = cu_count()) > 0) e = attn::launch_fwd_persistent(a, n_cu, st);
   else e = attn::launch_fwd_mfma(a, st);
   if (e == hipSuccess && p.n_split > 1) e = attn::launch_combine(a, st);

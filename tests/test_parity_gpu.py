@@ -92,12 +92,15 @@ def test_small_against_full_oracle(gpu_lib, case):
     assert_bf(o, lse, ro, rl, "full")
 
 
+@pytest.mark.parametrize("S_q", [70, 200])
 @pytest.mark.parametrize("n_split", [2, 3, 7])
 @pytest.mark.parametrize("dt,D,causal", [(torch.bfloat16, 128, True), (torch.bfloat16, 64, False),
                                           (torch.float16, 256, False), (torch.float32, 64, True)])
-def test_explicit_split_against_oracle(gpu_lib, n_split, dt, D, causal):
-    B, H, S_q, S_k = 1, 2, 70, 1000
-    note(f"split n={n_split} {dt} D{D} causal={causal}")
+def test_explicit_split_against_oracle(gpu_lib, n_split, dt, D, causal, S_q):
+    """Key-range splits: up to 128 query rows at D = 64 / 128 run on the short-range kernel, more rows on
+    the main kernel; D = 256 and float32 on their own kernels."""
+    B, H, S_k = 1, 2, 1000
+    note(f"split n={n_split} {dt} D{D} causal={causal} S_q{S_q}")
     q, k, v = inputs.qkv(B, H, S_q, S_k, D, seed=2, dtype=dt)
     scale = 1 / math.sqrt(D)
     o, lse = gpu_lib.fwd(q.cuda(), k.cuda(), v.cuda(), causal=causal, scale=scale, num_splits=n_split)
@@ -227,6 +230,15 @@ def test_fullsize_noncausal_d128_8k(gpu_lib):
 def test_fullsize_decode_32k(gpu_lib):
     note("full decode B64 H32 S_q1 S_k32768 D128")
     _fullsize(gpu_lib, 64, 32, 1, 32768, 128, False, heads=4)
+
+
+@pytest.mark.parametrize("S_q,D,causal", [(16, 128, False), (64, 64, True)])
+def test_fullsize_short_query_block_32k(gpu_lib, S_q, D, causal):
+    """A few query rows against 32K keys (B8 H32): the automatic key-range split on the short-range
+    kernel, sampled rows against the oracle."""
+    note(f"full short query block B8 H32 S_q{S_q} S_k32768 D{D} causal={causal}")
+    assert gpu_lib.num_splits(8, 32, S_q, 32768, D) > 1
+    _fullsize(gpu_lib, 8, 32, S_q, 32768, D, causal, heads=4)
 
 
 @pytest.mark.parametrize("dt,D", [(torch.bfloat16, 64), (torch.float16, 128), (torch.bfloat16, 256),

@@ -54,7 +54,8 @@ DENSE = [
     (1, 2, 300, 4500, 64, False, torch.bfloat16, None, "main kernel D64"),
     (1, 2, 2500, 2500, 128, True, torch.bfloat16, None, "persistent grid"),
     (1, 2, 600, 600, 256, True, torch.bfloat16, None, "D=256 kernel"),
-    (1, 2, 16, 9000, 128, False, torch.bfloat16, None, "split main kernel"),
+    (1, 2, 16, 9000, 128, False, torch.bfloat16, None, "split short-range kernel"),
+    (1, 2, 200, 9000, 128, False, torch.bfloat16, 3, "split main kernel"),
     (1, 2, 1, 9001, 128, False, torch.float16, None, "decode kernel"),
     (1, 2, 500, 1000, 128, True, torch.bfloat16, None, "short-range kernel"),
     (1, 2, 100, 333, 64, False, torch.float32, None, "float32 kernel"),
