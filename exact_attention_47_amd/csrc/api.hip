@@ -35,17 +35,33 @@ struct Plan {
   int keys_per_split;
 };
 
+constexpr int kChipCUs = 256;   // compute units of the MI355X
+
 Plan plan_splits(int dtype, int B, int H, int S_q, int S_k, int D, int req) {
-  (void)B; (void)H;
   const int tile = key_tile(dtype, D);
   const int n_tiles = (S_k + tile - 1) / tile;
   int n = 1;
   if (req > 1) {
     n = req;
   } else if (req == 0) {
-    // short query block against a long key range: split the keys so that
-    // many workgroups stream the key range in parallel
-    if (S_q <= 64 && S_k >= 8192) n = (S_k + 4095) / 4096;
+    if (S_q <= 64 && S_k >= 8192) {
+      // short query block against a long key range: split the keys so that
+      // many workgroups stream the key range in parallel
+      n = (S_k + 4095) / 4096;
+    } else if (S_k >= 8192) {
+      // too few 256-row query tiles to fill half the chip against a long key
+      // range: split the keys so that about one workgroup per compute unit
+      // runs, each split at least 2048 keys, with partial results that fit
+      // attn_fwd_noalloc's scratch (so both entry points plan alike)
+      const long long n_work = (long long)B * H * ((S_q + 255) / 256);
+      if (n_work < kChipCUs / 2) {
+        const long long per_split = (long long)B * H * S_q * (D + 1) * (long long)sizeof(float);
+        long long m = (kChipCUs + n_work - 1) / n_work;
+        m = std::min(m, (long long)(S_k + 2047) / 2048);
+        m = std::min(m, ((long long)ATTN_NOALLOC_SCRATCH_BYTES - 512) / per_split);
+        if (m > 1) n = (int)m;
+      }
+    }
   }
   if (n > n_tiles) n = n_tiles;
   if (n > 256) n = 256;

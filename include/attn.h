@@ -73,10 +73,13 @@ const char* attn_status_string(int status);
  *   dtype  ATTN_F32, ATTN_F16 or ATTN_BF16; accumulation is float32 in all cases
  *   D      64, 128 or 256 (ATTN_F32: 64 or 128)
  *
- * For short query lengths with long key ranges the library splits the key
- * range and merges the partial results by logsumexp; the temporary buffer it
- * needs is taken from the stream-ordered allocator on `stream` and released
- * on the same stream.
+ * Against long key ranges (8192 keys or more) the library splits the key
+ * range and merges the partial results by logsumexp when the query block is
+ * short (at most 64 rows) or the grid too small for the chip (fewer 256-row
+ * query tiles over all (b, h) than half its 256 compute units; then only as
+ * far as the partial results fit ATTN_NOALLOC_SCRATCH_BYTES). The temporary
+ * buffer it needs is taken from the stream-ordered allocator on `stream` and
+ * released on the same stream.
  */
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              int B, int H, int S_q, int S_k, int D, int causal, float scale,

@@ -90,6 +90,15 @@ def test_split_plan():
     # the decode shape splits its 32K keys; ordinary prefill does not
     assert attn.num_splits(64, 32, 1, 32768, 128) > 1
     assert attn.num_splits(2, 16, 8192, 8192, 128) == 1
+    # fewer 256-row query tiles than half the chip's CUs against 8K+ keys: a split whose partial results
+    # fit attn_fwd_noalloc's scratch, none where they would not, nor for short key ranges or full grids
+    for shape in ((1, 8, 1024, 65536, 128), (1, 2, 600, 9000, 128), (1, 1, 200, 8192, 256), (1, 32, 256, 32768, 64)):
+        assert attn.num_splits(*shape) > 1, shape
+        assert 0 < attn.workspace_size(*shape) <= attn.NOALLOC_SCRATCH_BYTES, shape
+    assert attn.num_splits(1, 8, 2048, 65536, 128) == 1
+    assert attn.num_splits(1, 2, 600, 8000, 128) == 1
+    assert attn.num_splits(1, 16, 16384, 16384, 128) == 1
+    assert attn.num_splits(2, 8, 8192, 8192, 256) == 1
     assert attn.num_splits(1, 1, 128, 128, 128, 1) == 1
     # requests are clamped to the number of key tiles (tiles hold at least 32 keys)
     # and never leave a split empty

@@ -109,6 +109,27 @@ def test_explicit_split_against_oracle(gpu_lib, n_split, dt, D, causal, S_q):
     assert_bf(o, lse, ro, rl, f"split {n_split}")
 
 
+@pytest.mark.parametrize("dt,D,causal,S_q,S_k", [(torch.bfloat16, 128, False, 600, 9000),
+                                                  (torch.bfloat16, 128, True, 600, 9000),
+                                                  (torch.bfloat16, 256, False, 200, 8192),
+                                                  (torch.float16, 64, True, 300, 8300),
+                                                  (torch.float32, 64, False, 150, 9000)])
+def test_low_occupancy_split_against_oracle(gpu_lib, dt, D, causal, S_q, S_k):
+    """attn_fwd splits the key range of a grid too small for the chip (here B1 H2) against 8K+ keys:
+    main-kernel, D = 256 and float32 splits and their merge against the full oracle."""
+    B, H = 1, 2
+    code = {torch.bfloat16: 2, torch.float16: 1, torch.float32: 0}[dt]
+    n = gpu_lib.num_splits(B, H, S_q, S_k, D, dtype=code)
+    note(f"low-occupancy split {dt} D{D} causal={causal} S_q{S_q} S_k{S_k}: {n} splits")
+    assert n > 1
+    q, k, v = inputs.qkv(B, H, S_q, S_k, D, seed=6, dtype=dt)
+    scale = 1 / math.sqrt(D)
+    o, lse = gpu_lib.fwd(q.cuda(), k.cuda(), v.cuda(), causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    ro, rl = oracle.attention(q.float().numpy(), k.float().numpy(), v.float().numpy(), causal, scale)
+    assert_bf(o, lse, ro, rl, f"low-occupancy split {n}")
+
+
 def test_decode_shape_small(gpu_lib):
     B, H, S_k, D = 2, 4, 9000, 128
     note("decode-like S_q=1 S_k=9000")

@@ -54,6 +54,21 @@ def test_noalloc_matches_attn_fwd_on_two_calls(gpu_lib):
             assert d.max() <= 1e-2 and np.sqrt(np.mean(d ** 2)) <= 2e-3 and le <= 1e-3
 
 
+def test_noalloc_low_occupancy_split(gpu_lib):
+    """A grid too small for the chip against a long key range: attn_fwd splits it within the scratch
+    array's size, so attn_fwd_noalloc takes the same split and gives the same bits."""
+    B, H, S_q, S_k, D = 1, 4, 700, 20000, 128
+    n = attn.num_splits(B, H, S_q, S_k, D)
+    note(f"noalloc low-occupancy split B{B} H{H} S_q{S_q} S_k{S_k}: {n} splits")
+    assert n > 1 and 0 < attn.workspace_size(B, H, S_q, S_k, D) <= attn.NOALLOC_SCRATCH_BYTES
+    q, k, v = inputs.qkv(B, H, S_q, S_k, D, seed=33, dtype=torch.bfloat16, device="cuda")
+    for causal in (False, True):
+        o_ref, l_ref = gpu_lib.fwd(q, k, v, causal=causal)
+        o, lse = gpu_lib.fwd_noalloc(q, k, v, causal=causal)
+        torch.cuda.synchronize()
+        assert torch.equal(o, o_ref) and torch.equal(lse, l_ref)
+
+
 def test_noalloc_without_split_and_refused_sizes(gpu_lib):
     note("noalloc: unsplit shape, then a split that would overflow the scratch array")
     q, k, v = inputs.qkv(1, 2, 300, 300, 128, seed=32, dtype=torch.bfloat16, device="cuda")
