@@ -110,7 +110,7 @@ def rne_expected(x32, dt):
 
 @pytest.mark.parametrize("dt", [torch.bfloat16, torch.float16])
 @pytest.mark.parametrize("S_k,D,what", [(2, 128, "short-range kernel"), (2048, 128, "main kernel"),
-                                        (8192, 64, "main kernel D64"), (256, 256, "D=256 kernel")])
+                                        (8192, 64, "split short-range kernel D64"), (256, 256, "D=256 kernel")])
 def test_output_rounds_to_nearest_even_at_midpoints(gpu_lib, dt, S_k, D, what):
     note(f"O rounding at midpoints, {what}, S_k={S_k} D={D} {dt}")
     S_q = 64

@@ -28,7 +28,8 @@ def note(msg):
 
 def test_noalloc_matches_attn_fwd_on_two_calls(gpu_lib):
     cases = [
-        # B, H, S_q, S_k, D, dtype: first the larger split (main kernel, 16 query rows), then a smaller one
+        # B, H, S_q, S_k, D, dtype: first the larger split (short-range kernel, 16 query rows), then a
+        # smaller one (decode kernel)
         (4, 8, 16, 12000, 128, torch.bfloat16),
         (2, 4, 1, 9000, 64, torch.float16),
     ]
