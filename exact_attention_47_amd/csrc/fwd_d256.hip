@@ -62,14 +62,14 @@ struct Cfg256 {
   static constexpr int NI = TILE / (NT * 16);   // direct-load instructions per thread per tile
   static constexpr int RPI = 1024 / RB;         // rows written by one wave instruction
   static_assert(TILE % (NT * 16) == 0, "tile must split evenly into 1 KiB wave loads");
-  static_assert(RPI * NW % 16 == 0, "a lane's rows must repeat the swizzle between its loads");
+  static_assert(RPI * NW % 8 == 0, "a lane's rows must step by a multiple of 8 between its loads");
 };
 
 constexpr float kTau256 = 8.0f;   // lazy-rescale threshold, log2 domain
 
 template <typename T, int D, int QB, int NW, int BN, bool CAUSAL, bool SPLIT, bool VARLEN>
 __global__ void __launch_bounds__(NW * 64)
-__attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
+__attribute__((amdgpu_waves_per_eu(2, 2)))   // two waves per SIMD: one 8-wave or two 4-wave workgroups per CU
 fwd_d256_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
                 T* __restrict__ O, float* __restrict__ LSE,
                 float* __restrict__ Opart, float* __restrict__ Lpart,
@@ -185,12 +185,18 @@ fwd_d256_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
   const int kv_bytes = VARLEN ? (S_k > 0 ? (S_k - 1) * RBg + C::RB : 0) : S_k * C::RB;
   const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)Kh, (short)0, kv_bytes, 0x00020000);
   const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)Vh, (short)0, kv_bytes, 0x00020000);
-  int lane_k, lane_v;
+  // with 4 waves a lane's rows step by 8 between its loads (ALT)
+  constexpr bool ALT = (C::RPI * C::NW) % 16 != 0;
+  static_assert(!(ALT && !SPLIT), "four-wave workgroups serve key-range splits only");
+  int lane_k, lane_k1, lane_v;
   {
     const int rsub = (lane * 16) / C::RB;
     const int u = ((lane * 16) % C::RB) / 16;
     const int r = wave * C::RPI + rsub;
     lane_k = rsub * RBg + ((u ^ (r & 15)) * 16);
+    // ALT: odd loads take the K swizzle of row r + 8 (the V swizzle repeats
+    // every 4 rows)
+    lane_k1 = ALT ? rsub * RBg + ((u ^ ((r + 8) & 15)) * 16) : lane_k;
     lane_v = rsub * RBg + ((u ^ (4 * (r & 3))) * 16);
   }
   // (offsets and destinations go through locals: a target builtin with
@@ -209,8 +215,14 @@ fwd_d256_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
         char* kdst = base + blk * 1024;
         char* vdst = base + C::TILE + blk * 1024;
         const int soff = (key0 + blk * C::RPI) * RBg;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (__attribute__((address_space(3))) void*)kdst, 16, lane_k,
-                                                 soff, 0, 0);
+        if constexpr (ALT) {
+          const int lk = (i & 1) ? lane_k1 : lane_k;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (__attribute__((address_space(3))) void*)kdst, 16, lk,
+                                                   soff, 0, 0);
+        } else {
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (__attribute__((address_space(3))) void*)kdst, 16, lane_k,
+                                                   soff, 0, 0);
+        }
         __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (__attribute__((address_space(3))) void*)vdst, 16, lane_v,
                                                  soff, 0, 0);
       }
@@ -227,7 +239,8 @@ fwd_d256_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
               __builtin_amdgcn_make_buffer_rsrc((void*)((const char*)Kh + off), (short)0, left, 0x00020000);
           const __amdgpu_buffer_rsrc_t v1 =
               __builtin_amdgcn_make_buffer_rsrc((void*)((const char*)Vh + off), (short)0, left, 0x00020000);
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(k1, (__attribute__((address_space(3))) void*)kdst, 16, lane_k,
+          const int lk = ALT && (i & 1) ? lane_k1 : lane_k;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(k1, (__attribute__((address_space(3))) void*)kdst, 16, lk,
                                                    0, 0, 0);
           __builtin_amdgcn_raw_ptr_buffer_load_lds(v1, (__attribute__((address_space(3))) void*)vdst, 16, lane_v,
                                                    0, 0, 0);
@@ -447,16 +460,27 @@ fwd_d256_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
 #define D256_BN 32
 #endif
 
-template <typename T, bool CAUSAL, bool SPLIT>
-static hipError_t launch_256(const FwdArgs& a, hipStream_t st) {
-  using C = Cfg256<256, 1, 8, D256_BN>;
+template <typename T, bool CAUSAL, bool SPLIT, int NW>
+static hipError_t launch_256_nw(const FwdArgs& a, hipStream_t st) {
+  using C = Cfg256<256, 1, NW, D256_BN>;
   if ((long long)(a.S_k + C::BN) * C::RB > 0x7fffffffLL) return hipErrorInvalidValue;   // 32-bit buffer offsets
   const int n_qt = (a.S_q + C::BM - 1) / C::BM;
   const int n_work = a.B * a.H * n_qt * a.n_split;
-  hipLaunchKernelGGL((fwd_d256_kernel<T, 256, 1, 8, D256_BN, CAUSAL, SPLIT, false>), dim3(n_work), dim3(C::NT), 0,
+  hipLaunchKernelGGL((fwd_d256_kernel<T, 256, 1, NW, D256_BN, CAUSAL, SPLIT, false>), dim3(n_work), dim3(C::NT), 0,
                      st, (const T*)a.q, (const T*)a.k, (const T*)a.v, (T*)a.o, a.lse, a.opart, a.lpart,
                      a.B * a.H, a.S_q, a.S_k, n_qt, a.n_split, a.keys_per_split, a.c, nullptr, nullptr, a.H, 0);
   return hipGetLastError();
+}
+
+// Eight-wave workgroups (256 rows); a key-range split of at most 128 query
+// rows runs on four-wave workgroups (128 rows, two per CU), which carry half
+// the idle rows (on full grids the eight-wave form is faster).
+template <typename T, bool CAUSAL, bool SPLIT>
+static hipError_t launch_256(const FwdArgs& a, hipStream_t st) {
+  if constexpr (SPLIT) {
+    if (a.S_q <= Cfg256<256, 1, 4, D256_BN>::BM) return launch_256_nw<T, CAUSAL, SPLIT, 4>(a, st);
+  }
+  return launch_256_nw<T, CAUSAL, SPLIT, 8>(a, st);
 }
 
 // packed batches: S_q / S_k are the longest sequences; the grid covers

@@ -253,10 +253,10 @@ def test_fullsize_decode_32k(gpu_lib):
     _fullsize(gpu_lib, 64, 32, 1, 32768, 128, False, heads=4)
 
 
-@pytest.mark.parametrize("S_q,D,causal", [(16, 128, False), (64, 64, True)])
+@pytest.mark.parametrize("S_q,D,causal", [(16, 128, False), (64, 64, True), (16, 256, False), (64, 256, True)])
 def test_fullsize_short_query_block_32k(gpu_lib, S_q, D, causal):
     """A few query rows against 32K keys (B8 H32): the automatic key-range split on the short-range
-    kernel, sampled rows against the oracle."""
+    kernel (D 64 / 128) or the D = 256 kernel's four-wave workgroups, sampled rows against the oracle."""
     note(f"full short query block B8 H32 S_q{S_q} S_k32768 D{D} causal={causal}")
     assert gpu_lib.num_splits(8, 32, S_q, 32768, D) > 1
     _fullsize(gpu_lib, 8, 32, S_q, 32768, D, causal, heads=4)
