@@ -37,8 +37,8 @@ struct Plan {
 
 constexpr int kChipCUs = 256;   // compute units of the MI355X
 
-Plan plan_splits(int dtype, int B, int H, int S_q, int S_k, int D, int req) {
-  const int tile = key_tile(dtype, D);
+// tile: the kernel's keys per tile; rows: query rows per workgroup
+Plan plan_core(int tile, int rows, int B, int H, int S_q, int S_k, int D, int req) {
   const int n_tiles = (S_k + tile - 1) / tile;
   int n = 1;
   if (req > 1) {
@@ -49,11 +49,11 @@ Plan plan_splits(int dtype, int B, int H, int S_q, int S_k, int D, int req) {
       // many workgroups stream the key range in parallel
       n = (S_k + 4095) / 4096;
     } else if (S_k >= 8192) {
-      // too few 256-row query tiles to fill half the chip against a long key
-      // range: split the keys so that about one workgroup per compute unit
-      // runs, each split at least 2048 keys, with partial results that fit
+      // too few query tiles to fill half the chip against a long key range:
+      // split the keys so that about one workgroup per compute unit runs,
+      // each split at least 2048 keys, with partial results that fit
       // attn_fwd_noalloc's scratch (so both entry points plan alike)
-      const long long n_work = (long long)B * H * ((S_q + 255) / 256);
+      const long long n_work = (long long)B * H * ((S_q + rows - 1) / rows);
       if (n_work < kChipCUs / 2) {
         const long long per_split = (long long)B * H * S_q * (D + 1) * (long long)sizeof(float);
         long long m = (kChipCUs + n_work - 1) / n_work;
@@ -70,6 +70,12 @@ Plan plan_splits(int dtype, int B, int H, int S_q, int S_k, int D, int req) {
   const int kps = tiles_per * tile;
   n = (S_k + kps - 1) / kps;          // drop splits that would be empty
   return Plan{n, kps};
+}
+
+// attn_fwd / attn_fwd_ex: the main kernel's 256-row workgroups at the
+// dtype's key tile (the short-range and D = 256 kernels' tiles divide it)
+Plan plan_splits(int dtype, int B, int H, int S_q, int S_k, int D, int req) {
+  return plan_core(key_tile(dtype, D), 256, B, H, S_q, S_k, D, req);
 }
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -482,9 +488,30 @@ int attn_fwd_fp8(const void* q8, const void* k8, const void* v8, const float* q_
   if (!aligned(q8, 16) || !aligned(k8, 16) || !aligned(v8, 16) || !aligned(o, 16) || !aligned(lse, 4) ||
       !aligned(q_scales, 4) || !aligned(k_scales, 4) || !aligned(v_scale, 4))
     return ATTN_ERR_MISALIGNED;
-  const hipError_t e = attn::launch_fwd_fp8(q8, k8, v8, q_scales, k_scales, v_scale, o, lse, B, H, S_q,
-                                            S_k, D, causal, scale * attn::kLog2e, v_transposed,
-                                            (hipStream_t)stream);
+  // key-range split by the rules of attn_fwd, at the FP8 kernel's 64-key
+  // tile and 128-row workgroups; the partials come from the stream-ordered
+  // allocator and are merged into o / lse by logsumexp
+  const Plan p = plan_core(attn::fp8_keys_per_tile(), attn::fp8_rows_per_block(), B, H, S_q, S_k, D, 0);
+  const hipStream_t st = (hipStream_t)stream;
+  const size_t need = ws_bytes(p, B, H, S_q, D);
+  void* buf = nullptr;
+  float *opart = nullptr, *lpart = nullptr;
+  if (need > 0) {
+    if (hipMallocAsync(&buf, need, st) != hipSuccess) return ATTN_ERR_LAUNCH;
+    const size_t rows = (size_t)p.n_split * B * H * S_q;
+    opart = (float*)buf;
+    lpart = (float*)((char*)buf + round_up(rows * D * sizeof(float), 256));
+  }
+  hipError_t e = attn::launch_fwd_fp8(q8, k8, v8, q_scales, k_scales, v_scale, o, lse, B, H, S_q, S_k, D, causal,
+                                      scale * attn::kLog2e, v_transposed, p.n_split, p.keys_per_split, opart, lpart,
+                                      st);
+  if (e == hipSuccess && p.n_split > 1) {
+    attn::FwdArgs a;
+    a.o = o; a.lse = lse; a.B = B; a.H = H; a.S_q = S_q; a.S_k = S_k; a.D = D;
+    a.dtype = ATTN_BF16; a.n_split = p.n_split; a.opart = opart; a.lpart = lpart;
+    e = attn::launch_combine(a, st);
+  }
+  if (need > 0 && hipFreeAsync(buf, st) != hipSuccess && e == hipSuccess) e = hipErrorUnknown;
   return e == hipSuccess ? ATTN_OK : (e == hipErrorNotSupported ? ATTN_ERR_UNSUPPORTED : ATTN_ERR_LAUNCH);
 }
 

@@ -114,12 +114,13 @@ template <int N> struct IC8 { static constexpr int value = N; };
 // at chunk position c ^ vt8_swz(d)
 __device__ __forceinline__ int vt8_swz(int d) { return (d >> 2) & 3; }
 
-template <bool CAUSAL, bool VT>
+template <bool CAUSAL, bool VT, bool SPLIT>
 __global__ void __launch_bounds__(NT8)
 __attribute__((amdgpu_waves_per_eu(3, 3)))
 fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ K8, const uint8_t* __restrict__ V8,
                const float* __restrict__ qs, const float* __restrict__ ks, const float* __restrict__ vs,
-               __bf16* __restrict__ O, float* __restrict__ LSE, int BH, int S_q, int S_k, int n_qt, float c)
+               __bf16* __restrict__ O, float* __restrict__ LSE, float* __restrict__ Opart, float* __restrict__ Lpart,
+               int BH, int S_q, int S_k, int n_qt, int n_split, int keys_per_split, float c)
 {
   __shared__ __attribute__((aligned(1024))) char st0[STAGE8];
   __shared__ __attribute__((aligned(1024))) char st1[STAGE8];
@@ -132,8 +133,15 @@ fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ K8, c
   const int nn = lane & 31;
 
   const int n_work = BH * n_qt;
-  int qt, bh;
-  if (CAUSAL && n_qt >= 16) {
+  int qt, bh, split = 0;
+  if (SPLIT) {
+    // key-range split: equal work per item, contiguous shares per XCD
+    int work = xcd_swizzle(blockIdx.x, n_work * n_split);
+    split = work % n_split;
+    work /= n_split;
+    qt = work % n_qt;
+    bh = work / n_qt;
+  } else if (CAUSAL && n_qt >= 16) {
     // query tiles heaviest first over all (b, h) at a time; consecutive
     // workgroups go to the 8 XCDs in turn, so (b, h) stays on XCD bh % 8
     // when B*H is a multiple of 8
@@ -148,9 +156,14 @@ fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ K8, c
   const int q0 = qt * BM8;
   const int wr0 = q0 + wave * 32;
   const int diag = S_k - S_q;
-  int k_end = S_k;
+  // this workgroup's keys: k_lo .. k_hi - 1 (a 64-key multiple apart), as
+  // tiles t0 .. t_end - 1 counted from key 0
+  const int k_lo = SPLIT ? split * keys_per_split : 0;
+  const int k_hi = SPLIT ? min(S_k, k_lo + keys_per_split) : S_k;
+  int k_end = k_hi;
   if (CAUSAL) k_end = min(k_end, q0 + BM8 - 1 + diag + 1);
-  const int n_tiles = k_end > 0 ? (k_end + BN8 - 1) / BN8 : 0;
+  const int t0 = k_lo / BN8;
+  const int t_end = k_end > k_lo ? (k_end + BN8 - 1) / BN8 : t0;
   const int nq_blk = (S_q + 63) / 64, nk_blk = (S_k + 63) / 64;
 
   const size_t qoff = (size_t)bh * S_q * D8;
@@ -272,7 +285,7 @@ fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ K8, c
     const int off = (min(t * BN8, S_k - 1) / 64) * 4;
     return c_q * __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ksrs, off, 0, 0));
   };
-  float cs_cur = c_q * ksh[0];
+  float cs_cur = c_q * ksh[t0];
 
   auto barrier = [] {
     asm volatile("" ::: "memory");
@@ -328,7 +341,7 @@ fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ K8, c
 #pragma unroll
           for (int jx = 0; jx < 4; jx++) {
             const int key = key0 + kb * 32 + 8 * i + 4 * hh + jx;
-            const bool ok = key < S_k && (!CAUSAL || key <= q + diag);
+            const bool ok = key < k_hi && (!CAUSAL || key <= q + diag);
             if (!ok) s[kb][4 * i + jx] = kNegInf;
           }
     }
@@ -401,23 +414,23 @@ fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ K8, c
     __builtin_amdgcn_s_waitcnt(0x0070 | 0x0F00 | (2 * NI8 + 1));   // stage t+1 complete
   };
 
-  if (n_tiles > 0) {
-    int t_last = n_tiles - 1;
+  if (t_end > t0) {
+    int t_last = t_end - 1;
     if (CAUSAL) {
       const int lim = wr0 + 31 + diag;
       t_last = lim < 0 ? -1 : min(t_last, lim / BN8);
     }
-    issue_stage(0, st0);
-    issue_stage(1, st1);
+    issue_stage(t0, st0);
+    issue_stage(t0 + 1, st1);
     __builtin_amdgcn_s_waitcnt(0x0070 | 0x0F00 | (2 * NI8));      // stage 0 complete
-    int u_mask = S_k / BN8;                      // tiles that need no mask for any row of the wave
+    int u_mask = k_hi / BN8;                     // tiles that need no mask for any row of the wave
     if (CAUSAL) {
       const int lim2 = wr0 + diag + 1;
       u_mask = min(u_mask, lim2 < 0 ? 0 : lim2 / BN8);
     }
     const IC8<0> P;
     const IC8<1> Mk;
-    int t = 0;
+    int t = t0;                                  // tile t sits in buffer (t - t0) % 3
     const int t_plain = min(t_last + 1, u_mask);  // tiles before this one need no mask
     for (; t + 2 < t_plain; t += 3) {
       step(IC8<0>(), P, t);
@@ -431,8 +444,8 @@ fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ K8, c
     }
     if (t <= t_last) { step(IC8<0>(), Mk, t); t++; }
     if (t <= t_last) { step(IC8<1>(), Mk, t); t++; }
-    for (; t < n_tiles; t++) {                   // the wave is done: keep the barriers and loads going
-      const int bsel = (t + 2) % 3;
+    for (; t < t_end; t++) {                     // the wave is done: keep the barriers and loads going
+      const int bsel = (t - t0 + 2) % 3;
       barrier();
       issue_stage(t + 2, bsel == 0 ? st0 : bsel == 1 ? st1 : st2);
       __builtin_amdgcn_s_waitcnt(0x0070 | 0x0F00 | (2 * NI8));
@@ -447,46 +460,85 @@ fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ K8, c
   const float inv = has ? v_scale / lt : 0.0f;
   const float lse = has ? (m + __builtin_log2f(lt) - kPShift8) * kLn2 : kNegInf;
   if (q < S_q) {
-    __bf16* orow = O + qoff + (size_t)q * D8;
+    if (!SPLIT) {
+      __bf16* orow = O + qoff + (size_t)q * D8;
 #pragma unroll
-    for (int db = 0; db < DB8; db++)
+      for (int db = 0; db < DB8; db++)
 #pragma unroll
-      for (int i = 0; i < 4; i++) {
-        typedef __bf16 v4b __attribute__((ext_vector_type(4)));
-        v4b w4;
+        for (int i = 0; i < 4; i++) {
+          typedef __bf16 v4b __attribute__((ext_vector_type(4)));
+          v4b w4;
 #pragma unroll
-        for (int j = 0; j < 4; j++) w4[j] = (__bf16)(o[db][4 * i + j] * inv);
-        *(v4b*)(orow + db * 32 + 8 * i + 4 * hh) = w4;
-      }
-    if (hh == 0) LSE[(size_t)bh * S_q + q] = lse;
+          for (int j = 0; j < 4; j++) w4[j] = (__bf16)(o[db][4 * i + j] * inv);
+          *(v4b*)(orow + db * 32 + 8 * i + 4 * hh) = w4;
+        }
+      if (hh == 0) LSE[(size_t)bh * S_q + q] = lse;
+    } else {
+      // this split's normalised partial output and LSE (merged by logsumexp)
+      const size_t prow = ((size_t)split * BH + bh) * S_q + q;
+      float* orow = Opart + prow * D8;
+#pragma unroll
+      for (int db = 0; db < DB8; db++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          float4 w;
+          w.x = o[db][4 * i + 0] * inv;
+          w.y = o[db][4 * i + 1] * inv;
+          w.z = o[db][4 * i + 2] * inv;
+          w.w = o[db][4 * i + 3] * inv;
+          *(float4*)(orow + db * 32 + 8 * i + 4 * hh) = w;
+        }
+      if (hh == 0) Lpart[prow] = lse;
+    }
   }
 }
 
 }  // namespace
 
-template <bool CAUSAL, bool VT>
-static void launch_fp8(dim3 grid, hipStream_t st, const void* q8, const void* k8, const void* v8, const float* qs,
-                       const float* ks, const float* vs, void* o, float* lse, int BH, int S_q, int S_k, int n_qt,
-                       float c) {
-  hipLaunchKernelGGL((fwd_fp8_kernel<CAUSAL, VT>), grid, dim3(NT8), 0, st, (const uint8_t*)q8, (const uint8_t*)k8,
-                     (const uint8_t*)v8, qs, ks, vs, (__bf16*)o, lse, BH, S_q, S_k, n_qt, c);
+struct Fp8Launch {
+  const void *q8, *k8, *v8;
+  const float *qs, *ks, *vs;
+  void* o;
+  float* lse;
+  float *opart, *lpart;
+  int BH, S_q, S_k, n_qt, n_split, keys_per_split;
+  float c;
+};
+
+template <bool CAUSAL, bool VT, bool SPLIT>
+static void launch_fp8(const Fp8Launch& a, hipStream_t st) {
+  const dim3 grid((unsigned)(a.BH * a.n_qt * (SPLIT ? a.n_split : 1)));
+  hipLaunchKernelGGL((fwd_fp8_kernel<CAUSAL, VT, SPLIT>), grid, dim3(NT8), 0, st, (const uint8_t*)a.q8,
+                     (const uint8_t*)a.k8, (const uint8_t*)a.v8, a.qs, a.ks, a.vs, (__bf16*)a.o, a.lse, a.opart,
+                     a.lpart, a.BH, a.S_q, a.S_k, a.n_qt, a.n_split, a.keys_per_split, a.c);
 }
+
+template <bool SPLIT>
+static void launch_fp8_s(const Fp8Launch& a, int causal, int v_transposed, hipStream_t st) {
+  if (causal) {
+    if (v_transposed) launch_fp8<true, true, SPLIT>(a, st);
+    else launch_fp8<true, false, SPLIT>(a, st);
+  } else {
+    if (v_transposed) launch_fp8<false, true, SPLIT>(a, st);
+    else launch_fp8<false, false, SPLIT>(a, st);
+  }
+}
+
+int fp8_keys_per_tile() { return BN8; }
+int fp8_rows_per_block() { return BM8; }
 
 hipError_t launch_fwd_fp8(const void* q8, const void* k8, const void* v8, const float* qs, const float* ks,
                           const float* vs, void* o, float* lse, int B, int H, int S_q, int S_k, int D,
-                          int causal, float c, int v_transposed, hipStream_t st) {
+                          int causal, float c, int v_transposed, int n_split, int keys_per_split, float* opart,
+                          float* lpart, hipStream_t st) {
   if (D != D8) return hipErrorNotSupported;
   if (v_transposed && S_k % 16 != 0) return hipErrorNotSupported;            // 16-byte aligned V^T rows
   if ((long long)(S_k + 4 * BN8) * D8 > 0x7fffffffLL) return hipErrorInvalidValue;   // 32-bit buffer offsets
-  const int n_qt = (S_q + BM8 - 1) / BM8;
-  const dim3 grid((unsigned)(B * H * n_qt));
-  if (causal) {
-    if (v_transposed) launch_fp8<true, true>(grid, st, q8, k8, v8, qs, ks, vs, o, lse, B * H, S_q, S_k, n_qt, c);
-    else launch_fp8<true, false>(grid, st, q8, k8, v8, qs, ks, vs, o, lse, B * H, S_q, S_k, n_qt, c);
-  } else {
-    if (v_transposed) launch_fp8<false, true>(grid, st, q8, k8, v8, qs, ks, vs, o, lse, B * H, S_q, S_k, n_qt, c);
-    else launch_fp8<false, false>(grid, st, q8, k8, v8, qs, ks, vs, o, lse, B * H, S_q, S_k, n_qt, c);
-  }
+  if (n_split > 1 && (keys_per_split % BN8 != 0 || !opart || !lpart)) return hipErrorInvalidValue;
+  Fp8Launch a{q8, k8, v8, qs, ks, vs, o, lse, opart, lpart, B * H, S_q, S_k, (S_q + BM8 - 1) / BM8,
+              n_split, keys_per_split, c};
+  if (n_split > 1) launch_fp8_s<true>(a, causal, v_transposed, st);
+  else launch_fp8_s<false>(a, causal, v_transposed, st);
   return hipGetLastError();
 }
 

@@ -91,10 +91,14 @@ hipError_t launch_rope_hadamard_quant(const void* x, void* x8, float* scales, co
                                       int rope_mode, int in_dtype, hipStream_t st);
 hipError_t launch_quant_per_tensor(const void* x, void* x8, float* scale, int B, int H, int S, int D,
                                    int in_dtype, int write_transposed, hipStream_t st);
+// n_split > 1: keys_per_split a multiple of fp8_keys_per_tile(); normalised
+// partial outputs / LSEs go to opart / lpart (merged by launch_combine)
 hipError_t launch_fwd_fp8(const void* q8, const void* k8, const void* v8, const float* qs,
                           const float* ks, const float* vs, void* o, float* lse, int B, int H,
                           int S_q, int S_k, int D, int causal, float c, int v_transposed,
-                          hipStream_t st);
+                          int n_split, int keys_per_split, float* opart, float* lpart, hipStream_t st);
+int fp8_keys_per_tile();
+int fp8_rows_per_block();
 
 // matrix-core stream for the roofline report (kind 0: bf16 32x32x16, 1: fp8
 // 32x32x64, 2: bf16 16x16x32), `blocks` workgroups of four waves, one float

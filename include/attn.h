@@ -330,7 +330,11 @@ int quant_per_tensor(const void* x, void* x8, float* scale, int B, int H, int S,
  * 2^7 (relative to the row's running reference, which moves when the row
  * grows by more than 1.75 in log2); the row sums are those of the rounded
  * values, so O is normalised by the weights that multiply V and the LSE is the
- * log of their sum. D = 128.
+ * log of their sum. D = 128. The key range is split and the partial results
+ * merged by logsumexp as attn_fwd does (at least 8192 keys, and a query block
+ * of at most 64 rows or fewer than 128 query tiles of 128 rows over all
+ * (b, h)); the merge buffer is taken from the stream-ordered allocator on
+ * `stream` and released on the same stream.
  */
 int attn_fwd_fp8(const void* q8, const void* k8, const void* v8,
                  const float* q_scales, const float* k_scales, const float* v_scale,

@@ -176,7 +176,7 @@ def test_fp8_attention_against_dequantized_oracle(gpu_lib, S_q, S_k, causal):
 
 
 @pytest.mark.parametrize("S_q,S_k,causal", [(300, 700, False), (520, 520, True), (130, 61, False),
-                                            (2100, 2100, True)])
+                                            (2100, 2100, True), (16, 9000, True), (200, 8300, False)])
 def test_fp8_attention_constant_v(gpu_lib, S_q, S_k, causal):
     """Constant V gives constant O: the kernel divides by the sum of the same rounded weights that
     multiply V, so O = c up to float32 accumulation and the bf16 rounding of O, on any scores (here
@@ -194,13 +194,45 @@ def test_fp8_attention_constant_v(gpu_lib, S_q, S_k, causal):
     assert err <= 1.75 * 2.0 ** -8
 
 
+@pytest.mark.parametrize("S_q,S_k,causal,transposed", [(1, 9000, False, False), (16, 9000, True, False),
+                                                       (200, 8300, False, False), (40, 9008, False, True)])
+def test_fp8_attention_split_against_dequantized_oracle(gpu_lib, S_q, S_k, causal, transposed):
+    """attn_fwd_fp8 splits the key range of short query blocks (at most 64 rows) and of grids too small
+    for the chip (here B1 H2) against 8K+ keys, and merges the splits' partials by logsumexp. Each split
+    rounds P against its own running reference, at a factor 2^k with k >= 7 for every p, and normalises
+    by its own rounded sum; the merge weights are those sums. So the bounds of the unsplit kernel hold:
+    per element oracle.p_rounding_bound plus half a bf16 step, per row oracle.p_rounding_lse_bound."""
+    note(f"fp8 split S_q{S_q} S_k{S_k} causal={causal} transposed V={transposed}")
+    B, H, D = 1, 2, 128
+    scale = 1 / math.sqrt(D)
+    q, k, v = inputs.qkv(B, H, S_q, S_k, D, seed=13, dtype=torch.bfloat16, outliers=True)
+    sg = inputs.signs(D, 13)
+    q8, qs = gpu_lib.hadamard_quant(q.cuda(), sg.cuda())
+    k8, ks = gpu_lib.hadamard_quant(k.cuda(), sg.cuda())
+    v8, vs = gpu_lib.quant_per_tensor(v.cuda(), transposed=transposed)
+    o, lse = gpu_lib.fwd_fp8(q8, k8, v8, qs, ks, vs, causal=causal, scale=scale, v_transposed=transposed)
+    torch.cuda.synchronize()
+    qf, kf, vf, sn = q.float().numpy(), k.float().numpy(), v.float().numpy(), sg.numpy()
+    qh, kh, vh = oracle.fp8_pipeline.dequantized_inputs(qf, kf, vf, "hadamard", sn)
+    ref, ref_lse = oracle.attention(qh, kh, vh, causal, scale)
+    err = np.abs(o.float().cpu().numpy() - ref)
+    bound = oracle.p_rounding_bound(qh, kh, vh, causal, scale)
+    limit = bound * (1 + 1e-2) + 2.0 ** -8 * (np.abs(ref) + bound) + 1e-6
+    lse_abs = np.abs(lse.cpu().numpy() - ref_lse)
+    lse_lim = oracle.p_rounding_lse_bound(qh, kh, causal, scale) * (1 + 1e-2) + 1e-5
+    print(f"    fp8 split: O max {err.max():.3e}, largest error / per-element limit {float((err / limit).max()):.3f}, "
+          f"LSE max {lse_abs.max():.3e} (largest / per-row limit {float((lse_abs / lse_lim).max()):.3f})", flush=True)
+    assert np.all(err <= limit)
+    assert np.all(lse_abs <= lse_lim)
+
+
 # fl32(ln 2): its float32 product with fl32(log2 e), the factor the library folds into the exponent,
 # is exactly 1, so the scores reach exp2 unchanged
 LN2_F32 = 0.6931471824645996
 
 
 @pytest.mark.parametrize("S_q,S_k,causal", [(300, 700, False), (520, 520, True), (130, 61, False),
-                                            (2100, 2100, True)])
+                                            (2100, 2100, True), (64, 8200, False), (300, 8192, True)])
 def test_fp8_attention_exact_arithmetic(gpu_lib, S_q, S_k, causal):
     """Inputs on which the FP8 kernel's arithmetic is exact: Q and K codes are small integers (so every
     score q8 . k8 is an integer), the block scales are 1 and scale * log2(e) is exactly 1, so every
