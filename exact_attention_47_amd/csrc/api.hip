@@ -51,8 +51,9 @@ Plan plan_core(int tile, int rows, int B, int H, int S_q, int S_k, int D, int re
     } else if (S_k >= 8192) {
       // too few query tiles to fill half the chip against a long key range:
       // split the keys so that about one workgroup per compute unit runs,
-      // each split at least 2048 keys, with partial results that fit
-      // attn_fwd_noalloc's scratch (so both entry points plan alike)
+      // into at most ceil(S_k / 2048) splits, with partial results that fit
+      // ATTN_NOALLOC_SCRATCH_BYTES (for attn_fwd: so that attn_fwd_noalloc
+      // plans alike; for attn_fwd_fp8: a modest merge buffer)
       const long long n_work = (long long)B * H * ((S_q + rows - 1) / rows);
       if (n_work < kChipCUs / 2) {
         const long long per_split = (long long)B * H * S_q * (D + 1) * (long long)sizeof(float);
@@ -72,8 +73,9 @@ Plan plan_core(int tile, int rows, int B, int H, int S_q, int S_k, int D, int re
   return Plan{n, kps};
 }
 
-// attn_fwd / attn_fwd_ex: the main kernel's 256-row workgroups at the
-// dtype's key tile (the short-range and D = 256 kernels' tiles divide it)
+// attn_fwd / attn_fwd_ex: 256-row workgroups at the key tile of the dtype
+// and D (the main kernel's 128 keys at D = 64 / 128, which the short-range
+// kernel's 32-key tile divides; the D = 256 and float32 kernels' own tiles)
 Plan plan_splits(int dtype, int B, int H, int S_q, int S_k, int D, int req) {
   return plan_core(key_tile(dtype, D), 256, B, H, S_q, S_k, D, req);
 }
