@@ -383,9 +383,12 @@ int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float*
   a.c = scale * attn::kLog2e;
   a.opart = nullptr; a.lpart = nullptr;
   a.cu_q = cu_seqlens_q; a.cu_k = cu_seqlens_k; a.total_q = total_q;
-  // D = 256 runs on its own kernel, D = 64 / 128 on the main one
+  // D = 256 runs on its own kernel; D = 64 / 128 on the short-range kernel
+  // when the longest key sequence is within its range (as for attn_fwd),
+  // else on the main one
   const hipError_t e = D == 256 ? attn::launch_fwd_d256_varlen(a, (hipStream_t)stream)
-                                : attn::launch_fwd_varlen(a, (hipStream_t)stream);
+                       : use_short_kernel(D, causal, max_seqlen_k, 1) ? attn::launch_fwd_short_varlen(a, (hipStream_t)stream)
+                                                                       : attn::launch_fwd_varlen(a, (hipStream_t)stream);
   if (e != hipSuccess) {
     rc = e == hipErrorInvalidValue ? ATTN_ERR_UNSUPPORTED : ATTN_ERR_LAUNCH;
     if (verbose()) fprintf(stderr, "[attn] varlen launch failed: %s\n", hipGetErrorString(e));

@@ -82,14 +82,16 @@ constexpr float kSumMax = 256.0f;   // lazy rescale: a lane's tile sum of P may 
 
 template <int N> struct IC { static constexpr int value = N; };
 
-template <typename T, int D, bool CAUSAL, bool SPLIT>
+template <typename T, int D, bool CAUSAL, bool SPLIT, bool VARLEN>
 __global__ void __launch_bounds__(256)
 __attribute__((amdgpu_waves_per_eu(D == 64 ? 4 : 3, D == 64 ? 4 : 3)))
 fwd_short_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
                 T* __restrict__ O, float* __restrict__ LSE,
                 float* __restrict__ Opart, float* __restrict__ Lpart,
-                int BH, int S_q, int S_k, int n_qt, int n_split, int keys_per_split, float c)
+                int BH, int S_q_, int S_k_, int n_qt, int n_split, int keys_per_split, float c,
+                const int* __restrict__ cu_q, const int* __restrict__ cu_k, int H, int total_q)
 {
+  static_assert(!(VARLEN && SPLIT), "packed batches run unsplit");
   using C = ShortCfg<D>;
   using M = Mma<T>;
   typedef typename M::frag frag;
@@ -107,7 +109,18 @@ fwd_short_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __re
 
   // ---- which (b*h, q tile, split) this workgroup computes
   int split = 0, qt, bh;
-  if (CAUSAL && !SPLIT && (D == 64 || n_qt >= 16)) {
+  if (VARLEN) {
+    // packed batches: XCD x takes heads x, x+8, ... one at a time with all
+    // their query tiles (highest first) when B*H is a multiple of 8
+    if (BH % 8 == 0) {
+      const int x = blockIdx.x % 8, j = blockIdx.x / 8;
+      bh = x + 8 * (j / n_qt);
+      qt = n_qt - 1 - j % n_qt;
+    } else {
+      qt = n_qt - 1 - (int)(blockIdx.x / BH);
+      bh = blockIdx.x % BH;
+    }
+  } else if (CAUSAL && !SPLIT && (D == 64 || n_qt >= 16)) {
     // query tiles heaviest first over all (b, h) at a time; consecutive
     // workgroups go to the 8 XCDs in turn, so (b, h) stays on XCD bh % 8
     // when B*H is a multiple of 8. Measured against the contiguous share of
@@ -128,6 +141,34 @@ fwd_short_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __re
 
   const int q0 = qt * C::BM;
   const int wr0 = q0 + wave * 32;              // first row of this wave
+
+  // ---- where this (b, h) lives. Dense: [B, H, S, D]. Packed: [total, H, D],
+  // sequence b at rows cu[b] .. cu[b+1]-1, rows H*D elements apart; LSE is
+  // [H, total_q].
+  int S_q = S_q_, S_k = S_k_;
+  const int pitch = VARLEN ? H * D : D;        // elements between consecutive rows
+  const T *Qh, *Kh, *Vh;
+  T* Oh;
+  float* lseh;
+  if (VARLEN) {
+    const int b = bh / H, h = bh % H;
+    const int q_beg = cu_q[b], k_beg = cu_k[b];
+    S_q = cu_q[b + 1] - q_beg;
+    S_k = cu_k[b + 1] - k_beg;
+    if (q0 >= S_q) return;                     // whole workgroup: past this sequence's rows
+    Qh = Q + ((size_t)q_beg * H + h) * D;
+    Kh = K + ((size_t)k_beg * H + h) * D;
+    Vh = V + ((size_t)k_beg * H + h) * D;
+    Oh = O + ((size_t)q_beg * H + h) * D;
+    lseh = LSE + (size_t)h * total_q + q_beg;
+  } else {
+    Qh = Q + (size_t)bh * S_q * D;
+    Kh = K + (size_t)bh * S_k * D;
+    Vh = V + (size_t)bh * S_k * D;
+    Oh = O + (size_t)bh * S_q * D;
+    lseh = LSE + (size_t)bh * S_q;
+  }
+  const int RBg = pitch * (int)sizeof(T);      // bytes between consecutive rows in memory
   const int diag = S_k - S_q;                  // causal: key j allowed iff j <= i + diag
   int k_lo = 0, k_hi = S_k;
   if (SPLIT) {
@@ -138,12 +179,6 @@ fwd_short_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __re
   if (CAUSAL) k_end = min(k_end, q0 + C::BM - 1 + diag + 1);
   const int n_tiles = k_end > k_lo ? (k_end - k_lo + C::BN - 1) / C::BN : 0;
 
-  const size_t qoff = (size_t)bh * S_q * D;
-  const size_t koff = (size_t)bh * S_k * D;
-  const T* Qh = Q + qoff;
-  const T* Kh = K + koff;
-  const T* Vh = V + koff;
-
   // ---- Q^T fragments (B operand of S^T), kept in registers
   frag qf[C::DS];
   {
@@ -151,7 +186,7 @@ fwd_short_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __re
 #pragma unroll
     for (int ds = 0; ds < C::DS; ds++) {
       if (q < S_q) {
-        qf[ds] = *(const frag*)(Qh + (size_t)q * D + ds * 16 + 8 * hh);
+        qf[ds] = *(const frag*)(Qh + (size_t)q * pitch + ds * 16 + 8 * hh);
       } else {
 #pragma unroll
         for (int e = 0; e < 8; e++) qf[ds][e] = (T)0.0f;
@@ -165,8 +200,10 @@ fwd_short_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __re
   // buffer loads on per-head resources: rows outside K/V read zeros (their
   // scores are masked, or the tile is never read), and every stage issues the
   // same number of instructions, which keeps the wait counts exact.
-  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)Kh, (short)0, S_k * C::RB, 0x00020000);
-  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)Vh, (short)0, S_k * C::RB, 0x00020000);
+  // (packed rows are RBg bytes apart; the range ends after the last row)
+  const int kv_bytes = VARLEN ? (S_k > 0 ? (S_k - 1) * RBg + C::RB : 0) : S_k * C::RB;
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)Kh, (short)0, kv_bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)Vh, (short)0, kv_bytes, 0x00020000);
   const int dma_rsub = (lane * 16) / C::RB;
   const int dma_u = ((lane * 16) % C::RB) / 16;
   // (offsets and destinations go through locals: a target builtin with
@@ -177,8 +214,8 @@ fwd_short_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __re
     for (int i = 0; i < C::NI; i++) {
       const int blk = i * C::NW + wave;
       const int r = blk * C::RPI + dma_rsub;
-      const int koff = (krow0 + r) * C::RB + ((dma_u ^ k_swz<D>(r)) * 16);
-      const int voff = (krow0 + r) * C::RB + ((dma_u ^ v_swz<D>(r)) * 16);
+      const int koff = (krow0 + r) * RBg + ((dma_u ^ k_swz<D>(r)) * 16);
+      const int voff = (krow0 + r) * RBg + ((dma_u ^ v_swz<D>(r)) * 16);
       char* kdst = base + blk * 1024;
       char* vdst = base + C::TILE + blk * 1024;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (__attribute__((address_space(3))) void*)kdst, 16, koff, 0, 0, 0);
@@ -400,7 +437,7 @@ fwd_short_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __re
   const float lse = has ? (m + __builtin_log2f(lt)) * kLn2 : kNegInf;
   if (q < S_q) {
     if (!SPLIT) {
-      T* orow = O + qoff + (size_t)q * D;
+      T* orow = Oh + (size_t)q * pitch;
 #pragma unroll
       for (int db = 0; db < C::DB; db++)
 #pragma unroll
@@ -411,7 +448,7 @@ fwd_short_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __re
           for (int j = 0; j < 4; j++) w[j] = (T)(o[db][4 * i + j] * inv);
           *(v4t*)(orow + db * 32 + 8 * i + 4 * hh) = w;
         }
-      if (hh == 0) LSE[(size_t)bh * S_q + q] = lse;
+      if (hh == 0) lseh[q] = lse;
     } else {
       const size_t prow = ((size_t)split * BH + bh) * S_q + q;
       float* orow = Opart + prow * D;
@@ -433,17 +470,34 @@ fwd_short_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __re
 
 // ---------------------------------------------------------------- launchers
 
-template <typename T, int D, bool CAUSAL, bool SPLIT>
+template <typename T, int D, bool CAUSAL, bool SPLIT, bool VARLEN = false>
 hipError_t launch_one(const FwdArgs& a, hipStream_t st) {
   using C = ShortCfg<D>;
-  // K and V are addressed per head through 32-bit buffer offsets
-  if ((long long)(a.S_k + 4 * C::BN) * C::RB > 0x7fffffffLL) return hipErrorInvalidValue;
+  // K and V are addressed per head through 32-bit buffer offsets (packed:
+  // over H*D-element row steps; S_k is then the longest key sequence)
+  const long long row_bytes = VARLEN ? (long long)a.H * C::RB : C::RB;
+  if ((long long)(a.S_k + 4 * C::BN) * row_bytes > 0x7fffffffLL) return hipErrorInvalidValue;
   const int n_qt = (a.S_q + C::BM - 1) / C::BM;
   const int n_work = a.B * a.H * n_qt * a.n_split;
-  hipLaunchKernelGGL((fwd_short_kernel<T, D, CAUSAL, SPLIT>), dim3(n_work), dim3(C::NT), 0, st,
+  hipLaunchKernelGGL((fwd_short_kernel<T, D, CAUSAL, SPLIT, VARLEN>), dim3(n_work), dim3(C::NT), 0, st,
                      (const T*)a.q, (const T*)a.k, (const T*)a.v, (T*)a.o, a.lse, a.opart, a.lpart,
-                     a.B * a.H, a.S_q, a.S_k, n_qt, a.n_split, a.keys_per_split, a.c);
+                     a.B * a.H, a.S_q, a.S_k, n_qt, a.n_split, a.keys_per_split, a.c, a.cu_q, a.cu_k, a.H,
+                     a.total_q);
   return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch_varlen_d(const FwdArgs& a, hipStream_t st) {
+  return a.causal ? launch_one<T, D, true, false, true>(a, st) : launch_one<T, D, false, false, true>(a, st);
+}
+
+template <typename T>
+hipError_t launch_varlen_t(const FwdArgs& a, hipStream_t st) {
+  switch (a.D) {
+    case 64: return launch_varlen_d<T, 64>(a, st);
+    case 128: return launch_varlen_d<T, 128>(a, st);
+  }
+  return hipErrorInvalidValue;
 }
 
 template <typename T, int D>
@@ -470,6 +524,12 @@ int short_rows_per_block() { return ShortCfg<128>::BM; }
 hipError_t launch_fwd_short(const FwdArgs& a, hipStream_t st) {
   if (a.dtype == 2) return launch_t<__bf16>(a, st);
   return launch_t<_Float16>(a, st);
+}
+
+hipError_t launch_fwd_short_varlen(const FwdArgs& a, hipStream_t st) {
+  if (a.n_split != 1) return hipErrorInvalidValue;
+  if (a.dtype == 2) return launch_varlen_t<__bf16>(a, st);
+  return launch_varlen_t<_Float16>(a, st);
 }
 
 }  // namespace attn

@@ -62,6 +62,8 @@ hipError_t launch_fwd_persistent(const FwdArgs& a, int n_wg, hipStream_t st);
 // short causal key ranges, D = 64 / 128 (two co-resident 4-wave workgroups per CU)
 hipError_t launch_fwd_short(const FwdArgs& a, hipStream_t st);
 int short_rows_per_block();
+// packed batches ([total, H, D] through cu_q / cu_k, unsplit)
+hipError_t launch_fwd_short_varlen(const FwdArgs& a, hipStream_t st);
 int short_keys_per_tile();
 
 // head dimension 256 (dense: called through launch_fwd_mfma; packed: from attn_fwd_varlen)

@@ -51,6 +51,12 @@ CASES = [
     ([7, 300, 129], [50, 300, 700], True),
     ([40, 10, 300], [20, 10, 260], True),
     ([5, 8], [0, 8], False),
+    # longest key sequence past the short-range kernel's range at D = 128 (and at D = 64 for the
+    # last case): the main kernel's packed form; the shorter cases above run on the short-range kernel
+    # at D = 64 / 128
+    ([1100, 2100, 50], [1100, 2100, 50], False),
+    ([300, 2300, 700], [900, 2300, 700], True),
+    ([4200, 100], [4200, 130], False),
 ]
 
 
@@ -68,13 +74,13 @@ def test_varlen_against_oracle(gpu_lib, case, dtype, D):
 
 
 @pytest.mark.parametrize("S,causal,D", [(2000, False, 128), (2500, True, 128), (700, False, 256),
-                                        (1100, True, 256)])
+                                        (1100, True, 256), (700, False, 128), (1500, True, 64)])
 def test_varlen_equal_lengths_bitwise_equal_dense(gpu_lib, S, causal, D):
     """B sequences of one length: the packed path gives the dense path's bits, transposed in layout.
 
-    (Lengths where the dense entry point runs the same kernel unsplit: the main kernel at D = 128
-    beyond the short-range kernel's ranges, whose different tiling changes the rounding order, and
-    the D = 256 kernel at any length here.)"""
+    (The packed and dense entry points pick the kernel alike: the main kernel at D = 128 beyond the
+    short-range kernel's ranges, the short-range kernel within them, the D = 256 kernel at any
+    length.)"""
     note(f"varlen vs dense S{S} causal={causal} D{D}")
     B, H = 2, 4
     q, k, v = inputs.qkv(B, H, S, S, D, seed=5, dtype=torch.bfloat16, device="cuda")
