@@ -199,6 +199,38 @@ def bwd_point(causal, B=2, H=16, S=8192, D=128, steps=10, warmup=3):
     return res
 
 
+def split_points(steps=10, warmup=3):
+    """Key-range splits chosen by the library for shapes whose grid alone would leave CUs idle: a small batch
+    against a long key range (bf16 B1 H8, 1024 rows, 64K keys), a short query block (bf16 B8 H32, 16 rows, 32K
+    keys) and FP8 decode (B1 H32, one row, 32K keys). Rate in TFLOP/s and K/V bytes streamed per second."""
+    out = []
+    for kind, B, H, S_q, S_k in (("bf16", 1, 8, 1024, 65536), ("bf16", 8, 32, 16, 32768), ("fp8", 1, 32, 1, 32768)):
+        D = 128
+        scale = 1 / math.sqrt(D)
+        q, k, v = inputs.qkv(B, H, S_q, S_k, D, seed=0, dtype=torch.bfloat16, device="cuda", outliers=kind == "fp8")
+        if kind == "bf16":
+            o, lse = attn.fwd(q, k, v, False, scale)
+            ms, _ = time_launches(lambda: attn.fwd(q, k, v, False, scale, out=o, lse=lse), steps, warmup)
+            n = attn.num_splits(B, H, S_q, S_k, D)
+            kv_bytes = 2 * B * H * S_k * D * 2
+        else:
+            sg = inputs.signs(D, 0).cuda()
+            q8, qs = attn.hadamard_quant(q, sg)
+            k8, ks = attn.hadamard_quant(k, sg)
+            v8, vs = attn.quant_per_tensor(v)
+            o, lse = attn.fwd_fp8(q8, k8, v8, qs, ks, vs, False, scale)
+            ms, _ = time_launches(lambda: attn.fwd_fp8(q8, k8, v8, qs, ks, vs, False, scale, out=o, lse=lse),
+                                  steps, warmup)
+            n = None
+            kv_bytes = 2 * B * H * S_k * D
+        fl = flops(B, H, S_q, S_k, D, False)
+        out.append({"dtype": kind, "B": B, "H": H, "S_q": S_q, "S_k": S_k, "D": D, "n_split": n, "ms": round(ms, 4),
+                    "tflops": round(fl / ms / 1e9, 1), "kv_gbps": round(kv_bytes / ms / 1e6, 1)})
+        del q, k, v, o, lse
+        torch.cuda.empty_cache()
+    return out
+
+
 def fp8_point(steps=10, warmup=3):
     """FP8 pipeline on the outlier workload: B=2, H=16, S=8K, D=128, non-causal."""
     B, H, S, D = 2, 16, 8192, 128
@@ -308,7 +340,7 @@ def main():
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["fp8", "decode", "d256", "causal_sweep", "d64_sweep", "varlen", "bwd",
-                                       "bwd_d64", "persistent"],
+                                       "bwd_d64", "persistent", "splits"],
                     default=None,
                     help="run just this extra workload and print its JSON (for profiling one kernel family)")
     ap.add_argument("--point", type=str, default=None, metavar="B,H,S_q,S_k,D,causal",
@@ -353,6 +385,7 @@ def main():
                                for c in (True, False)],
             "bwd": lambda: [bwd_point(c, steps=st, warmup=wu) for c in (False, True)],
             "bwd_d64": lambda: [bwd_point(c, B=4, H=32, S=4096, D=64, steps=st, warmup=wu) for c in (False, True)],
+            "splits": lambda: split_points(steps=st, warmup=wu),
             "persistent": lambda: persistent_points(steps=st, warmup=wu),
         }
         print(json.dumps({"only": args.only, "result": runs[args.only]()}), flush=True)
@@ -441,6 +474,7 @@ def main():
         extras["backward_d64_4k"] = [bwd_point(False, B=4, H=32, S=4096, D=64),
                                      bwd_point(True, B=4, H=32, S=4096, D=64)]
         extras["persistent_causal"] = persistent_points()
+        extras["key_range_splits"] = split_points()
         out["extras"] = extras
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(B, H, S, D, causal)
