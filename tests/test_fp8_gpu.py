@@ -226,6 +226,35 @@ def test_fp8_attention_split_against_dequantized_oracle(gpu_lib, S_q, S_k, causa
     assert np.all(lse_abs <= lse_lim)
 
 
+def test_fp8_attention_fullsize_decode_32k(gpu_lib):
+    """FP8 decode at full size (B1 H32, one query row, 32K keys, outlier inputs): the split path with its
+    merge, four heads against exact attention on the dequantized inputs, to the bounds of the split test."""
+    note("fp8 decode B1 H32 S_q1 S_k32768 D128 outliers")
+    B, H, S_k, D = 1, 32, 32768, 128
+    scale = 1 / math.sqrt(D)
+    q, k, v = inputs.qkv(B, H, 1, S_k, D, seed=0, dtype=torch.bfloat16, device="cuda", outliers=True)
+    sg = inputs.signs(D, 0).cuda()
+    o, lse = _pipeline(gpu_lib, q, k, v, sg, False, scale)
+    torch.cuda.synchronize()
+    amax = {"v": float(v.float().abs().max())}
+    sn = sg.cpu().numpy()
+    worst, worst_lse = 0.0, 0.0
+    for h in (0, 31, 9, 20):
+        qf, kf, vf = (x[0, h][None, None].float().cpu().numpy() for x in (q, k, v))
+        qh, kh, vh = oracle.fp8_pipeline.dequantized_inputs(qf, kf, vf, "hadamard", sn, amax=amax)
+        ref, ref_lse = oracle.attention(qh, kh, vh, False, scale)
+        err = np.abs(o[0, h][None, None].float().cpu().numpy() - ref)
+        bound = oracle.p_rounding_bound(qh, kh, vh, False, scale)
+        limit = bound * (1 + 1e-2) + 2.0 ** -8 * (np.abs(ref) + bound) + 1e-6
+        lse_abs = np.abs(lse[0, h][None, None].cpu().numpy() - ref_lse)
+        lse_lim = oracle.p_rounding_lse_bound(qh, kh, False, scale) * (1 + 1e-2) + 1e-5
+        worst = max(worst, float((err / limit).max()))
+        worst_lse = max(worst_lse, float((lse_abs / lse_lim).max()))
+        assert np.all(err <= limit), h
+        assert np.all(lse_abs <= lse_lim), h
+    print(f"    fp8 decode: largest error / per-element limit {worst:.3f}, LSE {worst_lse:.3f}", flush=True)
+
+
 # fl32(ln 2): its float32 product with fl32(log2 e), the factor the library folds into the exponent,
 # is exactly 1, so the scores reach exp2 unchanged
 LN2_F32 = 0.6931471824645996

@@ -262,6 +262,15 @@ def test_fullsize_short_query_block_32k(gpu_lib, S_q, D, causal):
     _fullsize(gpu_lib, 8, 32, S_q, 32768, D, causal, heads=4)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_fullsize_small_batch_64k(gpu_lib, causal):
+    """1024 query rows against 64K keys at B1 H8 (eight query tiles in all): the split for grids too small
+    for the chip, sampled rows of four heads against the oracle."""
+    note(f"full small batch B1 H8 S_q1024 S_k65536 D128 causal={causal}")
+    assert gpu_lib.num_splits(1, 8, 1024, 65536, 128) > 1
+    _fullsize(gpu_lib, 1, 8, 1024, 65536, 128, causal, heads=4)
+
+
 @pytest.mark.parametrize("dt,D", [(torch.bfloat16, 64), (torch.float16, 128), (torch.bfloat16, 256),
                                   (torch.bfloat16, 128)])
 @pytest.mark.parametrize("n_split", [2, 5, 13])
