@@ -351,7 +351,7 @@ def main():
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (each (b, h) is independent; "
+        print("bench.py measures one GPU: the library has no multi-GPU path (each (b, h) is independent; "
               "sharding would split B*H across GPUs with no communication). Run with --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
